@@ -1,0 +1,287 @@
+"""Benchmark of the 4/6 NVFP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+
+A step is one fos_quantize call (tensor-scale pass + fused 4/6 quantize kernel) on the
+weight workload 4096x12288 bf16 (1D 16-value row blocks, 4/6, round-to-nearest-even),
+the configuration the headline metric is quoted on.  Inputs are resident in HBM
+before timing; three input/output sets (> 256 MB of inputs) rotate so that no call
+finds its input in the 256 MB Infinity Cache.  Times come from HIP events on the
+stream the kernels are launched on (torch's current stream).
+
+Printed: ONE JSON line with the headline (quantize GB/s of algorithmic bytes), the
+roofline of the dominant kernel (the quantize kernel timed alone, given the tensor
+scale), the CPU oracle timed on a bounded sample, and the other hot-path rows
+(column-wise, Hadamard + stochastic rounding, 2D, dequantize, qlinear TFLOP/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, published (2.5 PFLOP/s)
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp4_block_quantization_amd", "csrc", f)
+                  for f in ("quantize.hip", "device_common.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def quant_bytes(rows, cols, n_out=1):
+    n = rows * cols
+    return 2 * n + n_out * (n // 2 + n // 16) + 4
+
+
+def time_loop(fn, steps, warmup, rotate):
+    """Average ms per call of fn(i) over `steps` calls after `warmup`, i rotating."""
+    import torch
+    for i in range(warmup):
+        fn(i % rotate)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(i % rotate)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+class QuantCase:
+    """Rotating input/output sets for one quantize configuration."""
+
+    def __init__(self, fos, x_cpu, cfg_kw, sets):
+        import torch
+        self.fos = fos
+        self.cfg = fos.make_config(**cfg_kw)
+        self.outputs = cfg_kw.get("outputs", ("row",))
+        R, C = x_cpu.shape
+        self.R, self.C = R, C
+        dev = "cuda:0"
+        self.x = [x_cpu.to(dev) for _ in range(sets)]
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.out = []
+        for _ in range(sets):
+            rd = rs = cd = cs = None
+            if "row" in self.outputs:
+                rd, rs = torch.empty(R, C // 2, **u8), torch.empty(R, C // 16, **u8)
+            if "col" in self.outputs:
+                cd, cs = torch.empty(C, R // 2, **u8), torch.empty(C, R // 16, **u8)
+            self.out.append((rd, rs, cd, cs))
+        self.t = [torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(sets)]
+        self.ws = fos.workspace(dev)
+        self.sets = sets
+
+    def step(self, i):
+        rd, rs, cd, cs = self.out[i]
+        self.fos.fos_quantize(self.cfg, self.x[i], rd, rs, cd, cs, self.t[i], self.ws)
+
+    def scaled(self, i):
+        rd, rs, cd, cs = self.out[i]
+        self.fos.fos_quantize_scaled(self.cfg, self.x[i], self.t[i], rd, rs, cd, cs)
+
+    def scale_only(self, i):
+        self.fos.fos_tensor_scale(self.cfg, self.x[i], self.t[i], self.ws)
+
+
+def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1):
+    R, C = x_cpu.shape
+    sets = min(8, max(3, -(-300 * 2 ** 20 // (2 * R * C))))   # > 256 MB of inputs rotate
+    case = QuantCase(fos, x_cpu, cfg_kw, sets)
+    ms = time_loop(case.step, steps, warmup, sets)
+    ms_k = time_loop(case.scaled, steps, warmup, sets)
+    ms_a = time_loop(case.scale_only, steps, warmup, sets)
+    b = quant_bytes(R, C, n_out)
+    row = {"workload": name, "shape": [R, C], "options": {k: (list(v) if isinstance(v, tuple) else v)
+                                                          for k, v in cfg_kw.items()},
+           "bytes": b, "ms_step": ms, "GBps_step": b / ms / 1e6,
+           "frac_step": b / ms / 1e6 / HBM_PEAK_GBS,
+           "ms_quant_kernel": ms_k, "GBps_quant_kernel": b / ms_k / 1e6,
+           "frac_quant_kernel": b / ms_k / 1e6 / HBM_PEAK_GBS,
+           "ms_scale_kernel": ms_a, "GBps_scale_kernel": 2 * R * C / ms_a / 1e6}
+    del case
+    return row
+
+
+def bench_dequant(fos, x_cpu, steps, warmup):
+    import torch
+    R, C = x_cpu.shape
+    dev = "cuda:0"
+    q = fos.quantize(x_cpu.to(dev))
+    rows = {}
+    for dt, name, ob in ((torch.bfloat16, "bf16", 2), (torch.float32, "f32", 4)):
+        sets = 3
+        outs = [torch.empty(R, C, dtype=dt, device=dev) for _ in range(sets)]
+        datas = [q.data.clone() for _ in range(sets)]
+        scs = [q.scales.clone() for _ in range(sets)]
+
+        def fn(i):
+            fos.fos_dequantize(datas[i], scs[i], q.tensor_scale, R, C, outs[i])
+        ms = time_loop(fn, steps, warmup, sets)
+        b = R * C // 2 + R * C // 16 + 4 + ob * R * C
+        rows[name] = {"bytes": b, "ms": ms, "GBps": b / ms / 1e6, "frac": b / ms / 1e6 / HBM_PEAK_GBS}
+        del outs
+    return rows
+
+
+def bench_qlinear(fos, x_cpu, w_cpu, steps, warmup):
+    import torch
+    dev = "cuda:0"
+    xq = fos.quantize(x_cpu.to(dev))
+    wq = fos.quantize(w_cpu.to(dev))
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def fn(i):
+        fos.fos_qlinear_fwd(xq.data, xq.scales, xq.tensor_scale, wq.data, wq.scales,
+                            wq.tensor_scale, M, N, K, y)
+    ms = time_loop(fn, max(3, steps // 4), max(2, warmup // 2), 1)
+    flops = 2 * M * N * K
+    return {"shape": [M, N, K], "flop": flops, "ms": ms, "TFLOPs": flops / ms / 1e9,
+            "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+
+
+def cpu_baseline(x_cpu, rows_sample):
+    """The oracle, as it stands, on a slice of the weight workload (its own amax)."""
+    import numpy as np
+    import torch
+    from oracle import nvfp4 as N
+    bits = x_cpu[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    N.quantize(bits, N.Config())
+    dt = time.perf_counter() - t0
+    b = quant_bytes(rows_sample, x_cpu.shape[1])
+    return {"value": b / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle quantize of {rows_sample} rows of the 4096x12288 weight "
+                      f"({rows_sample * x_cpu.shape[1]} values, tensor scale included), "
+                      f"{dt:.1f} s of single-threaded NumPy"}
+
+
+def traffic_for(kernel: str):
+    try:
+        rec = json.load(open(PMC_FILE))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_dispatch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None,
+                    help="profiling aid: run one piece (c2_step, c2_kernel, copy) and exit")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "layout is described in DESIGN.md and not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp4_block_quantization_amd import fos, workloads as W
+
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    x2 = W.make("c2")
+
+    if args.only is not None:
+        if args.only == "copy":
+            a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+            b = torch.empty_like(a)
+            for _ in range(args.steps):
+                b.copy_(a)
+            torch.cuda.synchronize()
+            log("copy: 268435456 bytes per dispatch")
+            return
+        case = QuantCase(fos, x2, {}, 3)
+        fn = case.step if args.only == "c2_step" else case.scaled
+        case.step(0); case.step(1); case.step(2)
+        for i in range(args.steps):
+            fn(i % 3)
+        torch.cuda.synchronize()
+        log(f"ran {args.only} x{args.steps}")
+        return
+
+    log("C2 weight quantize ...")
+    head = bench_quant(fos, "c2 weight 4096x12288, 1D rows, 4/6, RNE", x2, {}, args.steps, args.warmup)
+    rows = {"c2_quantize": head}
+    log(json.dumps(head))
+    log("C2 dequantize ...")
+    rows["c2_dequantize"] = bench_dequant(fos, x2, args.steps, args.warmup)
+    log("C1 ...")
+    rows["c1_quantize"] = bench_quant(fos, "c1 256x256, 1D rows, 4/6, RNE", W.make("c1"), {},
+                                      args.steps, args.warmup)
+    log("C3 ...")
+    rows["c3_row_col"] = bench_quant(fos, "c3 activation 8192x4096, row + column outputs",
+                                     W.make("c3"), {"outputs": ("row", "col")}, args.steps,
+                                     args.warmup, n_out=2)
+    log("C4a ...")
+    rows["c4a_rht_sr"] = bench_quant(fos, "c4a gradient 8192x4096, Hadamard + stochastic rounding",
+                                     W.make("c4a"), {"hadamard_seed": 0, "rounding": "sr",
+                                                     "sr_seed": 1234}, args.steps, args.warmup)
+    log("C4b ...")
+    rows["c4b_2d"] = bench_quant(fos, "c4b weight 12288x4096, 2D 16x16", W.make("c4b"),
+                                 {"block": "2d"}, args.steps, args.warmup)
+    log("C5 qlinear ...")
+    rows["c5_qlinear"] = bench_qlinear(fos, W.make("c5_x"), W.make("c5_w"), args.steps, args.warmup)
+    log(json.dumps(rows["c5_qlinear"]))
+
+    cpu = None
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline(x2, x2.shape[0])
+
+    kernel_gbps = head["GBps_quant_kernel"]
+    out = {
+        "metric": "4/6 NVFP4 quantize GB/s (bf16 in) & % HBM peak; qlinear fwd TFLOP/s",
+        "value": round(head["GBps_step"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "4/6 NVFP4 quantize of a 4096x12288 bf16 weight "
+                               "(N(0,0.02), 0.1% x50 outliers), 1D 16-value row blocks, RNE",
+                   "rows": 4096, "cols": 12288, "algorithmic_bytes_per_step": head["bytes"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "quant_rows_kernel (fos_quantize_scaled)",
+                     "achieved": round(kernel_gbps, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbps / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("quant_rows_kernel")},
+        "cpu_baseline": cpu,
+        "qlinear_TFLOPs": round(rows["c5_qlinear"]["TFLOPs"], 1),
+        "qlinear_frac_fp16_mfma_peak": round(rows["c5_qlinear"]["frac"], 4),
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+// C ABI of the 4/6 NVFP4 library: argument validation (before any HIP call) and
+// kernel dispatch.  See include/fos.h for the contract of every entry point.
+#include "../../include/fos.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr size_t kWorkspaceBytes = 256;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Sign mask of the random Hadamard transform: bit k of word 0 of
+// Philox4x32-10(key = seed, counter = 0) (Salmon et al., SC'11).
+uint32_t hadamard_mask(uint64_t seed) {
+  uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  return c0 & 0xffffu;
+}
+
+fos_status check_config(const fos_quant_config* cfg) {
+  if (!cfg) return FOS_E_NULL;
+  if (cfg->struct_size != sizeof(fos_quant_config)) return FOS_E_FLAGS;
+  if (cfg->rule > FOS_RULE_6ONLY || cfg->rounding > FOS_ROUND_STOCHASTIC ||
+      cfg->block > FOS_BLOCK_2D || cfg->hadamard > 1)
+    return FOS_E_FLAGS;
+  if (cfg->outputs == 0 || (cfg->outputs & ~(uint32_t)(FOS_OUT_ROWWISE | FOS_OUT_COLWISE)))
+    return FOS_E_FLAGS;
+  if (cfg->hadamard && (cfg->block == FOS_BLOCK_2D ||
+                        cfg->outputs == (FOS_OUT_ROWWISE | FOS_OUT_COLWISE)))
+    return FOS_E_FLAGS;
+  return FOS_OK;
+}
+
+bool wants_cols(const fos_quant_config* cfg) { return (cfg->outputs & FOS_OUT_COLWISE) != 0; }
+bool wants_rows(const fos_quant_config* cfg) { return (cfg->outputs & FOS_OUT_ROWWISE) != 0; }
+
+fos_status check_input(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
+  if (cols % 16) return FOS_E_SHAPE;
+  if ((wants_cols(cfg) || cfg->block == FOS_BLOCK_2D) && rows % 16) return FOS_E_SHAPE;
+  if (rows * cols > 0) {
+    if (!x) return FOS_E_NULL;
+    if (!aligned(x, 16)) return FOS_E_ALIGN;
+  }
+  return FOS_OK;
+}
+
+fos_status check_outputs(const fos_quant_config* cfg, int64_t rows, int64_t cols,
+                         const uint8_t* row_data, const uint8_t* row_scales,
+                         const uint8_t* col_data, const uint8_t* col_scales) {
+  if (rows * cols == 0) return FOS_OK;
+  if (wants_rows(cfg)) {
+    if (!row_data || !row_scales) return FOS_E_NULL;
+    if (!aligned(row_data, 8)) return FOS_E_ALIGN;
+  }
+  if (wants_cols(cfg)) {
+    if (!col_data || !col_scales) return FOS_E_NULL;
+    if (!aligned(col_data, 8)) return FOS_E_ALIGN;
+  }
+  return FOS_OK;
+}
+
+fos_status check_scale_and_workspace(const float* tscale, const void* ws, size_t ws_bytes) {
+  if (!tscale) return FOS_E_NULL;
+  if (!aligned(tscale, 4)) return FOS_E_ALIGN;
+  if (!ws || ws_bytes < kWorkspaceBytes || !aligned(ws, 4)) return FOS_E_WORKSPACE;
+  return FOS_OK;
+}
+
+fos::QuantArgs make_args(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols,
+                         const float* tscale, uint8_t* row_data, uint8_t* row_scales,
+                         uint8_t* col_data, uint8_t* col_scales) {
+  fos::QuantArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.rows = rows;
+  a.cols = cols;
+  a.tscale = tscale;
+  a.row_data = row_data;
+  a.row_scales = row_scales;
+  a.col_data = col_data;
+  a.col_scales = col_scales;
+  a.rht_mask = cfg->hadamard ? hadamard_mask(cfg->hadamard_seed) : 0u;
+  a.sr_k0 = (uint32_t)cfg->sr_seed;
+  a.sr_k1 = (uint32_t)(cfg->sr_seed >> 32);
+  a.four_over_six = cfg->rule == FOS_RULE_4OVER6;
+  a.sr = cfg->rounding == FOS_ROUND_STOCHASTIC;
+  a.two_d = cfg->block == FOS_BLOCK_2D;
+  a.rows_out = wants_rows(cfg);
+  a.cols_out = wants_cols(cfg);
+  a.hadamard = cfg->hadamard != 0;
+  return a;
+}
+
+fos_status launch_scale(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols,
+                        float* tscale, void* ws, hipStream_t s) {
+  const bool had = cfg->hadamard != 0;
+  const uint32_t mask = had ? hadamard_mask(cfg->hadamard_seed) : 0u;
+  const hipError_t e = fos::launch_tensor_scale(static_cast<const uint16_t*>(x), rows, cols, had,
+                                                had && wants_cols(cfg), mask,
+                                                static_cast<uint32_t*>(ws), tscale, s);
+  return e == hipSuccess ? FOS_OK : FOS_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fos_abi_version(void) { return FOS_ABI_VERSION; }
+
+const char* fos_status_string(fos_status s) {
+  switch (s) {
+    case FOS_OK: return "FOS_OK";
+    case FOS_E_NULL: return "FOS_E_NULL: required pointer is NULL";
+    case FOS_E_SHAPE: return "FOS_E_SHAPE: unsupported tensor shape";
+    case FOS_E_ALIGN: return "FOS_E_ALIGN: misaligned pointer";
+    case FOS_E_FLAGS: return "FOS_E_FLAGS: invalid or unsupported option";
+    case FOS_E_WORKSPACE: return "FOS_E_WORKSPACE: workspace missing or too small";
+    case FOS_E_HIP: return "FOS_E_HIP: HIP launch failed";
+  }
+  return "FOS_E_UNKNOWN";
+}
+
+size_t fos_workspace_bytes(void) { return kWorkspaceBytes; }
+
+fos_status fos_tensor_scale(const fos_quant_config* cfg, const void* x, int64_t rows,
+                            int64_t cols, float* tensor_scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  fos_status st = check_config(cfg);
+  if (st != FOS_OK) return st;
+  if ((st = check_input(cfg, x, rows, cols)) != FOS_OK) return st;
+  if ((st = check_scale_and_workspace(tensor_scale, workspace, workspace_bytes)) != FOS_OK)
+    return st;
+  return launch_scale(cfg, x, rows, cols, tensor_scale, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+fos_status fos_quantize_scaled(const fos_quant_config* cfg, const void* x, int64_t rows,
+                               int64_t cols, const float* tensor_scale, uint8_t* row_data,
+                               uint8_t* row_scales, uint8_t* col_data, uint8_t* col_scales,
+                               void* stream) {
+  fos_status st = check_config(cfg);
+  if (st != FOS_OK) return st;
+  if ((st = check_input(cfg, x, rows, cols)) != FOS_OK) return st;
+  if (!tensor_scale) return FOS_E_NULL;
+  if (!aligned(tensor_scale, 4)) return FOS_E_ALIGN;
+  if ((st = check_outputs(cfg, rows, cols, row_data, row_scales, col_data, col_scales)) != FOS_OK)
+    return st;
+  const fos::QuantArgs a =
+      make_args(cfg, x, rows, cols, tensor_scale, row_data, row_scales, col_data, col_scales);
+  return fos::launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FOS_OK
+                                                                                 : FOS_E_HIP;
+}
+
+fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols,
+                        uint8_t* row_data, uint8_t* row_scales, uint8_t* col_data,
+                        uint8_t* col_scales, float* tensor_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  fos_status st = check_config(cfg);
+  if (st != FOS_OK) return st;
+  if ((st = check_input(cfg, x, rows, cols)) != FOS_OK) return st;
+  if ((st = check_scale_and_workspace(tensor_scale, workspace, workspace_bytes)) != FOS_OK)
+    return st;
+  if ((st = check_outputs(cfg, rows, cols, row_data, row_scales, col_data, col_scales)) != FOS_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launch_scale(cfg, x, rows, cols, tensor_scale, workspace, s)) != FOS_OK) return st;
+  const fos::QuantArgs a =
+      make_args(cfg, x, rows, cols, tensor_scale, row_data, row_scales, col_data, col_scales);
+  return fos::launch_quantize(a, s) == hipSuccess ? FOS_OK : FOS_E_HIP;
+}
+
+fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales, const float* tensor_scale,
+                          int64_t rows, int64_t cols, int out_dtype, void* out, void* stream) {
+  if (out_dtype != FOS_OUT_F32 && out_dtype != FOS_OUT_BF16) return FOS_E_FLAGS;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
+  if (cols % 16) return FOS_E_SHAPE;
+  if (rows * cols == 0) return FOS_OK;
+  if (!data || !scales || !tensor_scale || !out) return FOS_E_NULL;
+  if (!aligned(data, 8) || !aligned(out, 16) || !aligned(tensor_scale, 4)) return FOS_E_ALIGN;
+  return fos::launch_dequantize(data, scales, tensor_scale, rows, cols, out_dtype == FOS_OUT_BF16,
+                                out, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
+fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
+                           const float* x_tensor_scale, const uint8_t* w_data,
+                           const uint8_t* w_scales, const float* w_tensor_scale, int64_t M,
+                           int64_t N, int64_t K, void* y_bf16, void* stream) {
+  if (M < 1 || N < 1 || K < 64 || K % 64 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return FOS_E_SHAPE;
+  if (N > kMaxElems / M || K > kMaxElems / M || K > kMaxElems / N) return FOS_E_SHAPE;
+  if (!x_data || !x_scales || !x_tensor_scale || !w_data || !w_scales || !w_tensor_scale ||
+      !y_bf16)
+    return FOS_E_NULL;
+  if (!aligned(x_data, 16) || !aligned(w_data, 16) || !aligned(x_scales, 4) ||
+      !aligned(w_scales, 4) || !aligned(y_bf16, 2) || !aligned(x_tensor_scale, 4) ||
+      !aligned(w_tensor_scale, 4))
+    return FOS_E_ALIGN;
+  return fos::launch_qlinear(x_data, x_scales, x_tensor_scale, w_data, w_scales, w_tensor_scale,
+                             M, N, K, static_cast<uint16_t*>(y_bf16),
+                             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+// Device-side building blocks for the 4/6 NVFP4 kernels (gfx950).
+//
+// Method: Four Over Six documentation page (Hugging Face transformers docs),
+// section "Four Over Six" -- each block's scale maps its largest magnitude to 6 or to
+// 4, whichever gives the lower error.  Format: Ultralytics glossary "FP4", opening
+// section (E2M1 values 0, 0.5, 1, 1.5, 2, 3, 4, 6) and section "How FP4 works"
+// (16 values per FP8 E4M3 scale, plus a per-tensor FP32 scale).
+//
+// Arithmetic per block and candidate c in {6, 4}, all fp32 round-to-nearest-even,
+// subnormals preserved (the library is built with -ffp-contract=off):
+//   u_c = 1 / (t*c)               (per tensor)
+//   r   = a * u_c                 (a = block max |x|; r = 0 when a == 0)
+//   S   = E4M3 RNE saturating(r), D = value(S), d = D * t
+//   inv = 1 / d, or 0 when d is zero or subnormal (every value becomes a signed 0)
+//   v_i = x_i * inv, code = E2M1 RNE(v_i) (hardware cvt, saturating at 6) or the
+//         stochastic rounding below
+//   e_i = fma(E(code_i), d, -x_i) (the exact error rounded once)
+//   err = sum_i e_i*e_i, sequential in i (2D: rows sequential, then pairwise)
+// and the block keeps candidate 4 iff err_4 < err_6.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fos {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kScaleDenom = 2688.0f;  // largest E4M3 (448) * largest E2M1 (6)
+constexpr float kMinNormal = 0x1p-126f;
+
+// ---- bf16 ----------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack16(const uint4& a, const uint4& b, float (&x)[16]) {
+  x[0] = bf16_lo(a.x);  x[1] = bf16_hi(a.x);  x[2] = bf16_lo(a.y);  x[3] = bf16_hi(a.y);
+  x[4] = bf16_lo(a.z);  x[5] = bf16_hi(a.z);  x[6] = bf16_lo(a.w);  x[7] = bf16_hi(a.w);
+  x[8] = bf16_lo(b.x);  x[9] = bf16_hi(b.x);  x[10] = bf16_lo(b.y); x[11] = bf16_hi(b.y);
+  x[12] = bf16_lo(b.z); x[13] = bf16_hi(b.z); x[14] = bf16_lo(b.w); x[15] = bf16_hi(b.w);
+}
+
+// Round a finite fp32 to bf16 (nearest, ties to even); result in the low 16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// ---- E4M3 (OCP "FN": bias 7, max 448) ------------------------------------------
+// Round r >= 0 (or +inf) to the nearest E4M3 value, ties to even, saturating to 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float r) {
+  r = fminf(r, 448.0f);
+  const uint32_t b = __float_as_uint(r);
+  // normal range (r >= 2^-6): keep 3 mantissa bits, RNE on the fp32 pattern;
+  // exponent re-biased from 127 to 7 (shift by 120 << 3 in the code domain).
+  const uint32_t rounded = b + 0x7ffffu + ((b >> 20) & 1u);
+  const uint32_t normal = (rounded >> 20) - (120u << 3);
+  // subnormal range: uniform steps of 2^-9; rintf rounds to nearest even.
+  const uint32_t sub = (uint32_t)rintf(r * 512.0f);
+  return r < 0x1p-6f ? sub : normal;
+}
+
+// Exact value of a non-negative E4M3 code: placing the 7 code bits at fp32 bits
+// 26..20 gives 2^(e-127)(1+m/8) (or m*2^-129 for e == 0); scaling by 2^120
+// re-biases the exponent to 7.
+__device__ __forceinline__ float e4m3_decode(uint32_t s) {
+  return __uint_as_float(s << 20) * 0x1p120f;
+}
+
+// ---- E2M1 hardware conversions (scale operand 1.0 = no scaling) ------------------
+// Two fp32 -> two E2M1 nibbles (round to nearest even, saturating at +-6, sign kept),
+// written into byte `SEL` of `old`: first value in the low nibble.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pk_fp4(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+// Byte `SEL` of `w` (two nibbles) -> two signed fp32 E2M1 values.
+template <int SEL>
+__device__ __forceinline__ f32x2 cvt_pk_f32_fp4(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// ---- Philox4x32-10 (Salmon et al., SC'11) ----------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+  }
+  return c;
+}
+
+// Stochastic-rounding draws of one block: byte i of the 16 Philox output bytes,
+// returned as k_i + 0.5 (exact in fp32).  Counter = (b_lo, b_hi, 0, stream).
+__device__ __forceinline__ void sr_draws(uint64_t block, uint32_t stream, uint32_t k0,
+                                         uint32_t k1, float (&kk)[16]) {
+  const uint4 w = philox4x32_10(make_uint4((uint32_t)block, (uint32_t)(block >> 32), 0u, stream),
+                                k0, k1);
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    kk[i] = (float)((words[i >> 2] >> (8 * (i & 3))) & 0xffu) + 0.5f;
+}
+
+// Stochastic rounding of f = |v| >= 0 onto the E2M1 grid.  Scaling by s in
+// {2, 1, 1/2} makes the grid spacing 1 inside f's interval ([0,2), [2,4), [4,6]);
+// p = fractional position (exact); round up iff (k + 0.5)/256 < p.  Returns the
+// magnitude code; g receives the grid value.
+__device__ __forceinline__ uint32_t e2m1_sr(float f, float kk, float& g) {
+  f = fminf(f, 6.0f);
+  const bool b0 = f < 2.0f, b1 = f < 4.0f;
+  const float s = b0 ? 2.0f : (b1 ? 1.0f : 0.5f);
+  const float si = b0 ? 0.5f : (b1 ? 1.0f : 2.0f);
+  const uint32_t off = b0 ? 0u : (b1 ? 2u : 4u);
+  const float y = f * s;
+  const float yl = floorf(y);
+  const float p = y - yl;
+  const float yq = (kk < p * 256.0f) ? yl + 1.0f : yl;
+  g = yq * si;
+  return (uint32_t)yq + off;
+}
+
+// ---- random-sign 16-point Hadamard transform ---------------------------------------
+// y_k = x_k * (+-1/4) (sign k from bit k of `mask`), then butterflies with strides
+// 1, 2, 4, 8: (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h).
+__device__ __forceinline__ void rht16(float (&y)[16], uint32_t mask) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) y[k] *= ((mask >> k) & 1u) ? -0.25f : 0.25f;
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      const float a = y[j], b = y[j + h];
+      y[j] = a + b;
+      y[j + h] = a - b;
+    }
+  }
+}
+
+// ---- one candidate scale for one 16-value block ------------------------------------
+struct Cand {
+  uint32_t s;     // E4M3 byte
+  uint32_t lo;    // nibbles of elements 0..7 (element 2k low nibble of byte k)
+  uint32_t hi;    // nibbles of elements 8..15
+  float err;      // sequential fp32 sum of squared errors
+  float d;        // block decode scale D * t
+};
+
+// Scale byte, decode scale and element reciprocal of a candidate (per block).
+__device__ __forceinline__ void cand_scale(float a, float t, float u, uint32_t& s, float& d,
+                                           float& inv) {
+  const float r = (a == 0.0f) ? 0.0f : a * u;
+  s = e4m3_encode(r);
+  d = e4m3_decode(s) * t;
+  inv = (d >= kMinNormal) ? 1.0f / d : 0.0f;
+}
+
+// Round-to-nearest-even codes of 16 values with the hardware conversion, and the
+// sequential squared error of the dequantized values.
+__device__ __forceinline__ void cand_codes_rne(const float (&x)[16], float d, float inv,
+                                               Cand& c) {
+  uint32_t lo = 0, hi = 0;
+  lo = cvt_pk_fp4<0>(lo, x[0] * inv, x[1] * inv);
+  lo = cvt_pk_fp4<1>(lo, x[2] * inv, x[3] * inv);
+  lo = cvt_pk_fp4<2>(lo, x[4] * inv, x[5] * inv);
+  lo = cvt_pk_fp4<3>(lo, x[6] * inv, x[7] * inv);
+  hi = cvt_pk_fp4<0>(hi, x[8] * inv, x[9] * inv);
+  hi = cvt_pk_fp4<1>(hi, x[10] * inv, x[11] * inv);
+  hi = cvt_pk_fp4<2>(hi, x[12] * inv, x[13] * inv);
+  hi = cvt_pk_fp4<3>(hi, x[14] * inv, x[15] * inv);
+  f32x2 e[8];
+  e[0] = cvt_pk_f32_fp4<0>(lo); e[1] = cvt_pk_f32_fp4<1>(lo);
+  e[2] = cvt_pk_f32_fp4<2>(lo); e[3] = cvt_pk_f32_fp4<3>(lo);
+  e[4] = cvt_pk_f32_fp4<0>(hi); e[5] = cvt_pk_f32_fp4<1>(hi);
+  e[6] = cvt_pk_f32_fp4<2>(hi); e[7] = cvt_pk_f32_fp4<3>(hi);
+  float err = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float e0 = __builtin_fmaf(e[j].x, d, -x[2 * j]);
+    err = err + e0 * e0;
+    const float e1 = __builtin_fmaf(e[j].y, d, -x[2 * j + 1]);
+    err = err + e1 * e1;
+  }
+  c.lo = lo;
+  c.hi = hi;
+  c.err = err;
+}
+
+// Stochastic-rounding codes (software) and the sequential squared error.
+__device__ __forceinline__ void cand_codes_sr(const float (&x)[16], float d, float inv,
+                                              const float (&kk)[16], Cand& c) {
+  uint32_t lo = 0, hi = 0;
+  float err = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float v = x[i] * inv;
+    float g;
+    const uint32_t m = e2m1_sr(fabsf(v), kk[i], g);
+    const uint32_t q = m | ((__float_as_uint(x[i]) >> 28) & 8u);
+    if (i < 8) lo |= q << (4 * i); else hi |= q << (4 * (i - 8));
+    const float e = __builtin_fmaf(g, d, -fabsf(x[i]));
+    err = err + e * e;
+  }
+  c.lo = lo;
+  c.hi = hi;
+  c.err = err;
+}
+
+// Per-lane 16-value block amax.
+__device__ __forceinline__ float amax16(const float (&x)[16]) {
+  float m0 = fmaxf(fabsf(x[0]), fabsf(x[1]));
+  float m1 = fmaxf(fabsf(x[2]), fabsf(x[3]));
+#pragma unroll
+  for (int i = 4; i < 16; i += 4) {
+    m0 = fmaxf(m0, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
+    m1 = fmaxf(m1, fmaxf(fabsf(x[i + 2]), fabsf(x[i + 3])));
+  }
+  return fmaxf(m0, m1);
+}
+
+// Quantize one 1D block with both candidates (or 6 alone) and return the winner.
+template <bool kFourOverSix, bool kSR>
+__device__ __forceinline__ Cand quantize_block(const float (&x)[16], float t, float u6,
+                                               float u4, const float (&kk)[16]) {
+  const float a = amax16(x);
+  Cand c6, c4;
+  float inv6, inv4;
+  cand_scale(a, t, u6, c6.s, c6.d, inv6);
+  if (kSR) cand_codes_sr(x, c6.d, inv6, kk, c6); else cand_codes_rne(x, c6.d, inv6, c6);
+  if (!kFourOverSix) return c6;
+  cand_scale(a, t, u4, c4.s, c4.d, inv4);
+  if (kSR) cand_codes_sr(x, c4.d, inv4, kk, c4); else cand_codes_rne(x, c4.d, inv4, c4);
+  return (c4.err < c6.err) ? c4 : c6;
+}
+
+}  // namespace fos

@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fos {
+
+struct QuantArgs {
+  const uint16_t* x;        // bf16 [rows][cols]
+  int64_t rows, cols;
+  const float* tscale;      // device fp32 t
+  uint8_t* row_data;        // [rows][cols/2]   (may be null when not requested)
+  uint8_t* row_scales;      // [rows][cols/16]
+  uint8_t* col_data;        // [cols][rows/2]
+  uint8_t* col_scales;      // [cols][rows/16]
+  uint32_t rht_mask;        // bit k set -> sign k of the Hadamard transform is -1
+  uint32_t sr_k0, sr_k1;    // Philox key for stochastic rounding
+  bool four_over_six;
+  bool sr;
+  bool two_d;
+  bool rows_out, cols_out;
+  bool hadamard;
+};
+
+// t = max|x| / 2688 into *tscale; ws = 2 zero-filled u32 (max cell, counter).
+hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bool hadamard,
+                               bool hadamard_cols, uint32_t rht_mask, uint32_t* ws,
+                               float* tscale, hipStream_t stream);
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
+                             int64_t rows, int64_t cols, bool bf16_out, void* out,
+                             hipStream_t stream);
+
+hipError_t launch_qlinear(const uint8_t* xd, const uint8_t* xs, const float* xt,
+                          const uint8_t* wd, const uint8_t* ws, const float* wt, int64_t M,
+                          int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+
+}  // namespace fos

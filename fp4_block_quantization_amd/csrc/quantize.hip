@@ -1,0 +1,245 @@
+// 4/6 NVFP4 quantization kernels (Four Over Six documentation page, section "Four
+// Over Six": per block, the scale maps the block maximum to 6 or to 4, whichever
+// gives the lower error; options: 2D block scaling, transposed inputs, random
+// Hadamard transform, stochastic rounding).
+//
+// Three kernels, all one-pass over the bf16 input with every 16-value block held in
+// one lane's registers while both candidates are evaluated:
+//   quant_rows_kernel  row-wise 1D output: the tensor is a flat run of 16-value
+//                      blocks; lane = block; two 16-byte loads, one 8-byte store of
+//                      nibbles and one scale byte per lane.
+//   quant_tile_kernel  column-wise output (optionally row-wise from the same read):
+//                      a 256x64 tile goes through LDS (XOR-swizzled 16-byte groups,
+//                      so column reads hit 32 distinct banks per wave); each lane then
+//                      reads two adjacent 16-row column blocks as 16 dwords.
+//   quant_2d_kernel    16x16 tiles: 16 lanes hold the 16 rows of a tile; tile max and
+//                      error sums use lane shuffles; column-wise output is the LDS
+//                      transpose of the same nibbles.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace fos {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct TensorConsts {
+  float t, u6, u4;
+};
+
+__device__ __forceinline__ TensorConsts tensor_consts(const float* tscale) {
+  TensorConsts c;
+  c.t = tscale[0];
+  c.u6 = 1.0f / (c.t * 6.0f);
+  c.u4 = 1.0f / (c.t * 4.0f);
+  return c;
+}
+
+__device__ __forceinline__ void store_block(uint8_t* data, uint8_t* scales, int64_t data_off,
+                                            int64_t scale_off, const Cand& c) {
+  *reinterpret_cast<uint2*>(data + data_off) = make_uint2(c.lo, c.hi);
+  scales[scale_off] = (uint8_t)c.s;
+}
+
+// ------------------------------------------------------------------ row-wise, 1D
+template <bool k46, bool kSR, bool kRHT>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
+  const TensorConsts tc = tensor_consts(a.tscale);
+  const uint4* __restrict__ x = reinterpret_cast<const uint4*>(a.x);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+    const uint4 w0 = x[2 * b], w1 = x[2 * b + 1];
+    float v[16];
+    unpack16(w0, w1, v);
+    if (kRHT) rht16(v, a.rht_mask);
+    float kk[16];
+    if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, kk);
+    const Cand c = quantize_block<k46, kSR>(v, tc.t, tc.u6, tc.u4, kk);
+    store_block(a.row_data, a.row_scales, 8 * b, b, c);
+  }
+}
+
+// ------------------------------------------------------------------ column-wise tiles
+constexpr int kTileR = 256, kTileC = 64;
+
+template <bool k46, bool kSR, bool kRHT, bool kRows>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
+  // 256 rows x 32 dwords (64 bf16); logical dword q of row r lives at q ^ sw(r),
+  // sw(r) = 4 * ((r >> 4) & 7).
+  __shared__ uint32_t lds[kTileR * 32];
+  const int64_t R = a.rows, C = a.cols;
+  const int64_t tiles_c = (C + kTileC - 1) / kTileC;
+  const int64_t R0 = (int64_t)(blockIdx.x / tiles_c) * kTileR;
+  const int64_t C0 = (int64_t)(blockIdx.x % tiles_c) * kTileC;
+  const int tid = threadIdx.x;
+  const TensorConsts tc = tensor_consts(a.tscale);
+
+  const int j = tid & 3;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = (tid >> 2) + 64 * k;
+    const int64_t gr = R0 + row, gc = C0 + 16 * j;
+    const bool ok = gr < R && gc < C;
+    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+    if (ok) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
+      w0 = p[0];
+      w1 = p[1];
+    }
+    const int sw = 4 * ((row >> 4) & 7);
+    *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j) ^ sw)]) = w0;
+    *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j + 4) ^ sw)]) = w1;
+    if (kRows && ok) {
+      float v[16];
+      unpack16(w0, w1, v);
+      float kk[16];
+      const int64_t blk = gr * (C / 16) + gc / 16;
+      if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, kk);
+      const Cand c = quantize_block<k46, kSR>(v, tc.t, tc.u6, tc.u4, kk);
+      store_block(a.row_data, a.row_scales, 8 * blk, blk, c);
+    }
+  }
+  __syncthreads();
+
+  const int rb = tid & 15;
+  const int sw = 4 * (rb & 7);
+  const int64_t nrb = R / 16;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = (tid >> 4) + 16 * h;
+    const int64_t gr0 = R0 + 16 * rb, gc = C0 + 2 * p;
+    if (gr0 >= R || gc >= C) continue;
+    float va[16], vb[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = lds[(16 * rb + i) * 32 + (p ^ sw)];
+      va[i] = bf16_lo(w);
+      vb[i] = bf16_hi(w);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float (&v)[16] = s ? vb : va;
+      const int64_t col = gc + s;
+      if (kRHT) rht16(v, a.rht_mask);
+      const int64_t blk = col * nrb + gr0 / 16;
+      float kk[16];
+      if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, kk);
+      const Cand c = quantize_block<k46, kSR>(v, tc.t, tc.u6, tc.u4, kk);
+      store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 2D 16x16 tiles
+template <bool k46, bool kSR, bool kRows, bool kCols>
+__global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
+  __shared__ uint2 tr[16][17];
+  const int64_t R = a.rows, C = a.cols;
+  const int64_t tiles_c = C / 16;
+  const int64_t wg_per_row = (tiles_c + 15) / 16;
+  const int64_t R0 = (int64_t)(blockIdx.x / wg_per_row) * 16;
+  const int tid = threadIdx.x;
+  const int row = tid & 15, tl = tid >> 4;
+  const int64_t T = (int64_t)(blockIdx.x % wg_per_row) * 16 + tl;
+  const bool valid = T < tiles_c;
+  const TensorConsts tc = tensor_consts(a.tscale);
+
+  float v[16];
+  if (valid) {
+    const uint4* p = reinterpret_cast<const uint4*>(a.x + (R0 + row) * C + 16 * T);
+    unpack16(p[0], p[1], v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+  }
+  float kk[16];
+  const int64_t rblk = (R0 + row) * tiles_c + T;    // row-wise block id of this row
+  if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, kk);
+
+  float am = amax16(v);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+
+  Cand c6, c4;
+  float inv6, inv4;
+  cand_scale(am, tc.t, tc.u6, c6.s, c6.d, inv6);
+  if (kSR) cand_codes_sr(v, c6.d, inv6, kk, c6); else cand_codes_rne(v, c6.d, inv6, c6);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) c6.err = c6.err + __shfl_xor(c6.err, m);
+  Cand c = c6;
+  if (k46) {
+    cand_scale(am, tc.t, tc.u4, c4.s, c4.d, inv4);
+    if (kSR) cand_codes_sr(v, c4.d, inv4, kk, c4); else cand_codes_rne(v, c4.d, inv4, c4);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) c4.err = c4.err + __shfl_xor(c4.err, m);
+    if (c4.err < c6.err) c = c4;
+  }
+  if (kRows && valid) store_block(a.row_data, a.row_scales, 8 * rblk, rblk, c);
+  if (kCols) {
+    tr[tl][row] = make_uint2(c.lo, c.hi);
+    __syncthreads();
+    if (valid) {
+      const int cc = row;                      // this lane now owns column cc of the tile
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint2 q = tr[tl][i];
+        const uint32_t word = (cc < 8) ? q.x : q.y;
+        const uint32_t nib = (word >> (4 * (cc & 7))) & 0xfu;
+        if (i < 8) lo |= nib << (4 * i); else hi |= nib << (4 * (i - 8));
+      }
+      const int64_t col = 16 * T + cc;
+      const int64_t cblk = col * (R / 16) + R0 / 16;
+      *reinterpret_cast<uint2*>(a.col_data + 8 * cblk) = make_uint2(lo, hi);
+      a.col_scales[cblk] = (uint8_t)c.s;
+    }
+  }
+}
+
+template <bool k46, bool kSR>
+hipError_t dispatch_2d(const QuantArgs& a, hipStream_t s) {
+  const int64_t tiles_c = a.cols / 16;
+  const int64_t grid = (a.rows / 16) * ((tiles_c + 15) / 16);
+  if (a.rows_out && a.cols_out)
+    quant_2d_kernel<k46, kSR, true, true><<<grid, kThreads, 0, s>>>(a);
+  else if (a.rows_out)
+    quant_2d_kernel<k46, kSR, true, false><<<grid, kThreads, 0, s>>>(a);
+  else
+    quant_2d_kernel<k46, kSR, false, true><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <bool k46, bool kSR, bool kRHT>
+hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
+  if (!a.cols_out) {
+    const int64_t nblk = a.rows * a.cols / 16;
+    int64_t grid = (nblk + kThreads - 1) / kThreads;
+    if (grid > (int64_t)1 << 30) grid = (int64_t)1 << 30;
+    quant_rows_kernel<k46, kSR, kRHT><<<grid, kThreads, 0, s>>>(a, nblk);
+    return hipGetLastError();
+  }
+  const int64_t grid = ((a.rows + kTileR - 1) / kTileR) * ((a.cols + kTileC - 1) / kTileC);
+  if (a.rows_out)
+    quant_tile_kernel<k46, kSR, kRHT, true><<<grid, kThreads, 0, s>>>(a);
+  else
+    quant_tile_kernel<k46, kSR, kRHT, false><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <bool k46, bool kSR>
+hipError_t dispatch_rule(const QuantArgs& a, hipStream_t s) {
+  if (a.two_d) return dispatch_2d<k46, kSR>(a, s);
+  return a.hadamard ? dispatch_1d<k46, kSR, true>(a, s) : dispatch_1d<k46, kSR, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.four_over_six)
+    return a.sr ? dispatch_rule<true, true>(a, s) : dispatch_rule<true, false>(a, s);
+  return a.sr ? dispatch_rule<false, true>(a, s) : dispatch_rule<false, false>(a, s);
+}
+
+}  // namespace fos

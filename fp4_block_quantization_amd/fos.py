@@ -1,0 +1,244 @@
+"""Thin ctypes binding of libfos.so (the C ABI declared in include/fos.h).
+
+Argument marshalling only: every step of quantize / dequantize / qlinear runs in the
+library's HIP kernels.  PyTorch provides device memory and the current HIP stream.
+There is no fallback: if libfos.so is missing or fails to load, importing this
+module raises.
+
+Low-level functions carry the C names (fos_quantize, fos_dequantize, ...) and take
+device tensors; ``quantize`` / ``dequantize`` / ``qlinear_fwd`` allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfos.so")
+
+FOS_OK, FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_WORKSPACE, FOS_E_HIP = range(7)
+FOS_RULE_4OVER6, FOS_RULE_6ONLY = 0, 1
+FOS_ROUND_RNE, FOS_ROUND_STOCHASTIC = 0, 1
+FOS_BLOCK_1D, FOS_BLOCK_2D = 0, 1
+FOS_OUT_ROWWISE, FOS_OUT_COLWISE = 1, 2
+FOS_OUT_F32, FOS_OUT_BF16 = 0, 1
+
+
+class FosError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib.fos_status_string(status).decode()} (status {status})")
+
+
+class FosQuantConfig(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("rule", ctypes.c_uint32),
+                ("rounding", ctypes.c_uint32), ("block", ctypes.c_uint32),
+                ("outputs", ctypes.c_uint32), ("hadamard", ctypes.c_uint32),
+                ("hadamard_seed", ctypes.c_uint64), ("sr_seed", ctypes.c_uint64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m fp4_block_quantization_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(FosQuantConfig)
+    sigs = {
+        "fos_abi_version": ([], ctypes.c_int),
+        "fos_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "fos_workspace_bytes": ([], SZ),
+        "fos_tensor_scale": ([cfgp, P, I64, I64, P, P, SZ, P], ctypes.c_int),
+        "fos_quantize_scaled": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
+        "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
+        "fos_qlinear_fwd": ([P, P, P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+ABI_VERSION = _lib.fos_abi_version()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != FOS_OK:
+        raise FosError(status, what)
+
+
+def make_config(rule: str = "4/6", rounding: str = "rne", block: str = "1d",
+                outputs: Sequence[str] = ("row",), hadamard_seed: Optional[int] = None,
+                sr_seed: Optional[int] = None) -> FosQuantConfig:
+    rules = {"4/6": FOS_RULE_4OVER6, "6": FOS_RULE_6ONLY}
+    roundings = {"rne": FOS_ROUND_RNE, "sr": FOS_ROUND_STOCHASTIC}
+    blocks = {"1d": FOS_BLOCK_1D, "2d": FOS_BLOCK_2D}
+    out = 0
+    for o in outputs:
+        out |= {"row": FOS_OUT_ROWWISE, "col": FOS_OUT_COLWISE}[o]
+    if rounding == "sr" and sr_seed is None:
+        raise ValueError("stochastic rounding needs sr_seed")
+    return FosQuantConfig(ctypes.sizeof(FosQuantConfig), rules[rule], roundings[rounding],
+                          blocks[block], out, 0 if hadamard_seed is None else 1,
+                          0 if hadamard_seed is None else int(hadamard_seed) & (2 ** 64 - 1),
+                          0 if sr_seed is None else int(sr_seed) & (2 ** 64 - 1))
+
+
+_workspaces = {}
+
+
+def workspace(device: torch.device) -> torch.Tensor:
+    """Zero-filled workspace for the current stream of ``device`` (one per stream;
+    the library leaves it zero-filled after every call)."""
+    device = torch.device(device)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.zeros(int(_lib.fos_workspace_bytes()), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------- C-named wrappers
+
+def fos_tensor_scale(cfg: FosQuantConfig, x: torch.Tensor, tensor_scale: torch.Tensor,
+                     ws: Optional[torch.Tensor] = None) -> None:
+    ws = workspace(x.device) if ws is None else ws
+    _check(_lib.fos_tensor_scale(ctypes.byref(cfg), _ptr(x), x.shape[0], x.shape[1],
+                                 _ptr(tensor_scale), _ptr(ws), ws.numel(), _stream(x.device)),
+           "fos_tensor_scale")
+
+
+def fos_quantize_scaled(cfg: FosQuantConfig, x: torch.Tensor, tensor_scale: torch.Tensor,
+                        row_data=None, row_scales=None, col_data=None, col_scales=None) -> None:
+    _check(_lib.fos_quantize_scaled(ctypes.byref(cfg), _ptr(x), x.shape[0], x.shape[1],
+                                    _ptr(tensor_scale), _ptr(row_data), _ptr(row_scales),
+                                    _ptr(col_data), _ptr(col_scales), _stream(x.device)),
+           "fos_quantize_scaled")
+
+
+def fos_quantize(cfg: FosQuantConfig, x: torch.Tensor, row_data, row_scales, col_data,
+                 col_scales, tensor_scale: torch.Tensor,
+                 ws: Optional[torch.Tensor] = None) -> None:
+    ws = workspace(x.device) if ws is None else ws
+    _check(_lib.fos_quantize(ctypes.byref(cfg), _ptr(x), x.shape[0], x.shape[1],
+                             _ptr(row_data), _ptr(row_scales), _ptr(col_data), _ptr(col_scales),
+                             _ptr(tensor_scale), _ptr(ws), ws.numel(), _stream(x.device)),
+           "fos_quantize")
+
+
+def fos_dequantize(data: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Tensor,
+                   rows: int, cols: int, out: torch.Tensor) -> None:
+    dt = {torch.float32: FOS_OUT_F32, torch.bfloat16: FOS_OUT_BF16}[out.dtype]
+    _check(_lib.fos_dequantize(_ptr(data), _ptr(scales), _ptr(tensor_scale), rows, cols, dt,
+                               _ptr(out), _stream(out.device)), "fos_dequantize")
+
+
+def fos_qlinear_fwd(x_data, x_scales, x_t, w_data, w_scales, w_t, M: int, N: int, K: int,
+                    y: torch.Tensor) -> None:
+    _check(_lib.fos_qlinear_fwd(_ptr(x_data), _ptr(x_scales), _ptr(x_t), _ptr(w_data),
+                                _ptr(w_scales), _ptr(w_t), M, N, K, _ptr(y), _stream(y.device)),
+           "fos_qlinear_fwd")
+
+
+# ---------------------------------------------------------------- tensor-level API
+
+@dataclass
+class NVFP4Tensor:
+    """One NVFP4 record: data [R, C/2] nibbles, scales [R, C/16] E4M3 bytes, and the
+    per-tensor fp32 scale (device tensor of one element).  ``layout`` is "row" for
+    the row-wise record of X and "col" for the record of X^T."""
+    data: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+    layout: str = "row"
+    block: str = "1d"
+    hadamard_seed: Optional[int] = None
+
+    @property
+    def shape(self) -> Tuple[int, int]:
+        return (self.data.shape[0], self.data.shape[1] * 2)
+
+
+def _check_input(x: torch.Tensor):
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 CUDA tensor")
+
+
+def tensor_scale(x: torch.Tensor, hadamard_seed: Optional[int] = None,
+                 outputs: Sequence[str] = ("row",)) -> torch.Tensor:
+    _check_input(x)
+    cfg = make_config(outputs=outputs, hadamard_seed=hadamard_seed)
+    t = torch.empty(1, dtype=torch.float32, device=x.device)
+    fos_tensor_scale(cfg, x, t)
+    return t
+
+
+def quantize(x: torch.Tensor, rule: str = "4/6", rounding: str = "rne", block: str = "1d",
+             outputs: Sequence[str] = ("row",), hadamard_seed: Optional[int] = None,
+             sr_seed: Optional[int] = None, tensor_scale: Optional[torch.Tensor] = None
+             ) -> Union[NVFP4Tensor, Tuple[NVFP4Tensor, NVFP4Tensor]]:
+    """4/6 NVFP4 quantization of a bf16 [R, C] tensor.  Returns the row-wise record,
+    the column-wise record (quantization of X^T), or both as (row, col).  With
+    ``tensor_scale`` given (device fp32 [1]) the amax pass is skipped."""
+    _check_input(x)
+    cfg = make_config(rule, rounding, block, outputs, hadamard_seed, sr_seed)
+    R, C = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    rd = rs = cd = cs = None
+    if "row" in outputs:
+        rd, rs = torch.empty(R, C // 2, **u8), torch.empty(R, C // 16, **u8)
+    if "col" in outputs:
+        cd, cs = torch.empty(C, R // 2, **u8), torch.empty(C, R // 16, **u8)
+    if tensor_scale is None:
+        t = torch.empty(1, dtype=torch.float32, device=dev)
+        fos_quantize(cfg, x, rd, rs, cd, cs, t)
+    else:
+        t = tensor_scale
+        fos_quantize_scaled(cfg, x, t, rd, rs, cd, cs)
+    res = []
+    if rd is not None:
+        res.append(NVFP4Tensor(rd, rs, t, "row", block, hadamard_seed))
+    if cd is not None:
+        res.append(NVFP4Tensor(cd, cs, t, "col", block, hadamard_seed))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    R, C = q.shape
+    out = torch.empty(R, C, dtype=dtype, device=q.data.device)
+    fos_dequantize(q.data, q.scales, q.tensor_scale, R, C, out)
+    return out
+
+
+def qlinear_fwd(xq: NVFP4Tensor, wq: NVFP4Tensor) -> torch.Tensor:
+    """Y = deq(Xq) deq(Wq)^T in bf16; Xq [M, K] and Wq [N, K] row-wise records."""
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=xq.data.device)
+    fos_qlinear_fwd(xq.data, xq.scales, xq.tensor_scale, wq.data, wq.scales, wq.tensor_scale,
+                    M, N, K, y)
+    return y

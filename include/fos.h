@@ -1,0 +1,168 @@
+/*
+ * fos.h -- C ABI of the Four Over Six (4/6) NVFP4 library for AMD MI355X (gfx950).
+ *
+ * Method (Four Over Six documentation page, Hugging Face transformers docs,
+ * section "Four Over Six"): every NVFP4 block is scaled adaptively so that its
+ * largest magnitude maps either to 6 or to 4, whichever gives the lower quantization
+ * error; the options listed there are a random Hadamard transform, 2D block scaling,
+ * transposed inputs and stochastic rounding.  Format (Ultralytics glossary "FP4",
+ * section "How FP4 works"): 16 E2M1 values share one FP8 E4M3 scale, and the tensor
+ * carries a second FP32 scale.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or keeps a pointer after returning.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous: the status reports argument validation and
+ *     launch errors only; faults in the kernels surface at the caller's next sync.
+ *   - Validation runs before any HIP call; a non-FOS_OK status means nothing was
+ *     launched and no output was touched.
+ *   - Tensors are row-major and contiguous.  Element (r, c) of a [rows, cols] bf16
+ *     tensor is at byte offset 2*(r*cols + c).
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
+ *   - Calls are thread-safe; concurrent calls must not share a workspace.
+ *
+ * NVFP4 record layout (one orientation):
+ *   data   [R][C/2] bytes: byte k of a row holds element 2k in its low nibble and
+ *          element 2k+1 in its high nibble; a nibble is sign<<3 | magnitude code,
+ *          codes 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6 (E2M1, exponent bias 1).
+ *   scales [R][C/16] bytes: OCP E4M3 ("FN", bias 7, max 448) block scales.
+ *   t      one fp32 per tensor, decode direction: value = E2M1 * (E4M3 * t).
+ * Row-wise output: R = rows, C = cols (16-blocks along a row).
+ * Column-wise output ("transposed inputs"): the quantization of X^T: R = cols,
+ * C = rows (16-blocks of 16 consecutive rows of one column of X).
+ */
+#ifndef FOS_H
+#define FOS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FOS_ABI_VERSION 1
+
+typedef enum {
+  FOS_OK = 0,
+  FOS_E_NULL = 1,      /* a required pointer is NULL                                */
+  FOS_E_SHAPE = 2,     /* negative size, or a size that must be a multiple of 16
+                          (or of 64 for the qlinear K) is not                       */
+  FOS_E_ALIGN = 3,     /* bf16 input not 16-byte aligned, packed data not 8-byte
+                          aligned, or an output buffer misaligned                   */
+  FOS_E_FLAGS = 4,     /* unknown enum value, wrong struct_size, or an unsupported
+                          option combination (e.g. Hadamard with 2D blocks)         */
+  FOS_E_WORKSPACE = 5, /* workspace NULL or smaller than fos_workspace_bytes()      */
+  FOS_E_HIP = 6        /* a HIP launch failed                                        */
+} fos_status;
+
+/* Block-scale rule.  FOS_RULE_4OVER6: per block, keep the candidate (block max ->
+ * 6, or block max -> 4) with the lower squared error; ties go to 6.
+ * FOS_RULE_6ONLY: standard NVFP4, block max -> 6 (Ultralytics glossary "FP4",
+ * "How FP4 works"). */
+enum { FOS_RULE_4OVER6 = 0, FOS_RULE_6ONLY = 1 };
+/* E2M1 rounding: nearest-even, or stochastic (one Philox4x32-10 draw per block,
+ * 8 random bits per element; the pages list stochastic rounding as an option and
+ * the FP4 glossary's training section uses it for gradients). */
+enum { FOS_ROUND_RNE = 0, FOS_ROUND_STOCHASTIC = 1 };
+/* 1D: 16 consecutive values share a scale.  2D: a 16x16 tile shares one scale and
+ * one 4-vs-6 decision; its byte is written into all 16 row-block slots of the tile
+ * (the 1D scale layout is kept). */
+enum { FOS_BLOCK_1D = 0, FOS_BLOCK_2D = 1 };
+/* Output orientations (bitmask; at least one). */
+enum { FOS_OUT_ROWWISE = 1, FOS_OUT_COLWISE = 2 };
+/* Dequantize output element type. */
+enum { FOS_OUT_F32 = 0, FOS_OUT_BF16 = 1 };
+
+typedef struct {
+  uint32_t struct_size;   /* must equal sizeof(fos_quant_config)                    */
+  uint32_t rule;          /* FOS_RULE_*                                             */
+  uint32_t rounding;      /* FOS_ROUND_*                                            */
+  uint32_t block;         /* FOS_BLOCK_*                                            */
+  uint32_t outputs;       /* FOS_OUT_ROWWISE | FOS_OUT_COLWISE                      */
+  uint32_t hadamard;      /* 0, or 1 = random-sign 16-point Hadamard transform of
+                             every 1D block before quantization (one orientation
+                             only; not with 2D)                                      */
+  uint64_t hadamard_seed; /* Philox key for the 16 signs                            */
+  uint64_t sr_seed;       /* Philox key for stochastic rounding                     */
+} fos_quant_config;       /* host struct, read only during the call                 */
+
+/* ABI version of the loaded library (FOS_ABI_VERSION). */
+int fos_abi_version(void);
+
+/* Human-readable name of a status (static string, never NULL). */
+const char* fos_status_string(fos_status status);
+
+/* Bytes of device workspace that fos_tensor_scale / fos_quantize need.  The caller
+ * zero-fills the workspace once before its first use (e.g. hipMemset); every
+ * successful call leaves it zero-filled again. */
+size_t fos_workspace_bytes(void);
+
+/* Per-tensor scale.  Writes t = RN_fp32(A / 2688) to *tensor_scale (device fp32),
+ * where A = max |x| over the tensor -- over the transformed values when
+ * cfg->hadamard is set, in the orientation of the single requested output -- and
+ * 2688 = 448 * 6 (largest E4M3 value times largest E2M1 value).  The pages give
+ * only "a second per-tensor FP32 scale" (Ultralytics glossary "FP4", "How FP4
+ * works"); the constant is this library's reading.
+ *   x: bf16 [rows][cols], 16-byte aligned.  rows, cols >= 0; cols % 16 == 0;
+ *      rows % 16 == 0 when cfg requests a column-wise Hadamard transform.
+ *   An empty tensor gives t = 0.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_WORKSPACE,
+ * FOS_E_HIP. */
+fos_status fos_tensor_scale(const fos_quant_config* cfg, const void* x, int64_t rows,
+                            int64_t cols, float* tensor_scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* 4/6 quantization given the tensor scale (device fp32, e.g. from
+ * fos_tensor_scale, or the all-reduced maximum of per-shard scales).
+ *   row_data [rows][cols/2], row_scales [rows][cols/16]: required iff
+ *     cfg->outputs has FOS_OUT_ROWWISE, else ignored.  row_data 8-byte aligned.
+ *   col_data [cols][rows/2], col_scales [cols][rows/16]: required iff
+ *     FOS_OUT_COLWISE, else ignored.  col_data 8-byte aligned.
+ *   cols % 16 == 0; rows % 16 == 0 for column-wise output or 2D blocks.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_HIP. */
+fos_status fos_quantize_scaled(const fos_quant_config* cfg, const void* x, int64_t rows,
+                               int64_t cols, const float* tensor_scale,
+                               uint8_t* row_data, uint8_t* row_scales,
+                               uint8_t* col_data, uint8_t* col_scales, void* stream);
+
+/* fos_tensor_scale followed by fos_quantize_scaled on the same stream; the tensor
+ * scale is written to *tensor_scale. */
+fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows,
+                        int64_t cols, uint8_t* row_data, uint8_t* row_scales,
+                        uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dequantize one NVFP4 record: out[r][c] = RN_fp32(E2M1(q) * RN_fp32(E4M3(s) * t))
+ * with the nibble's sign (-0 for code 8); FOS_OUT_BF16 rounds that fp32 value to
+ * bf16 (nearest-even).  Works for row-wise, column-wise (giving X^T) and 2D records.
+ *   data [rows][cols/2] (8-byte aligned), scales [rows][cols/16], tensor_scale: one
+ *   device fp32; out [rows][cols] (16-byte aligned).  cols % 16 == 0.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_HIP. */
+fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales,
+                          const float* tensor_scale, int64_t rows, int64_t cols,
+                          int out_dtype, void* out, void* stream);
+
+/* Simulated quantized linear forward (Four Over Six documentation page, "Four Over
+ * Six": without native FP4 matmuls the layer is simulated with a higher-precision
+ * matrix multiplication of the dequantized operands):
+ *   Y[m][n] = bf16( (t_x * t_w) * sum_k (E*D)_x[m][k] * (E*D)_w[n][k] )
+ * Operands are row-wise NVFP4 records blocked along K: Xq [M][K] (x_data
+ * [M][K/2], x_scales [M][K/16]) and Wq [N][K] (the [out][in] Linear layout).
+ * E*D products are formed exactly in fp16, multiplied on the matrix cores with fp32
+ * accumulation; the tensor scales are applied in fp32 before the bf16 rounding.
+ *   M, N >= 1; K >= 64 and K % 64 == 0.  x_data, w_data 16-byte aligned;
+ *   y_bf16 [M][N], 4-byte aligned with N even... any N is accepted: y is written
+ *   with 2-byte stores at the edges.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
+                           const float* x_tensor_scale, const uint8_t* w_data,
+                           const uint8_t* w_scales, const float* w_tensor_scale,
+                           int64_t M, int64_t N, int64_t K, void* y_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOS_H */

@@ -16,3 +16,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def root_dir():
     return ROOT
+
+
+def pytest_sessionstart(session):
+    """On a host without a GPU, build libfos.so if it is missing so that the C ABI
+    checks can load it (on a GPU host the in-tree build is used as shipped)."""
+    lib = os.path.join(ROOT, "fp4_block_quantization_amd", "libfos.so")
+    if not os.path.exists(lib) and not os.path.exists("/dev/kfd"):
+        from fp4_block_quantization_amd.build import build
+        build(verbose=False)

@@ -1,0 +1,111 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point that
+include/fos.h declares, and rejects bad arguments with the documented status before
+any HIP call (the pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp4_block_quantization_amd import fos
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "fos.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fos_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", fos.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fos_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(fos.lib(), n) is not None
+
+
+def test_abi_version_and_strings():
+    assert fos.ABI_VERSION == 1
+    for s in range(7):
+        assert fos.lib().fos_status_string(s).startswith(b"FOS_")
+    assert fos.lib().fos_workspace_bytes() >= 8
+
+
+FAKE = ctypes.c_void_p(0x100000)          # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p(0x100002)
+
+
+def cfg(**kw):
+    c = fos.make_config(**{k: v for k, v in kw.items() if k != "raw"})
+    for k, v in kw.get("raw", {}).items():
+        setattr(c, k, v)
+    return c
+
+
+def q(c, x=FAKE, rows=64, cols=64, rd=FAKE, rs=FAKE, cd=FAKE, cs=FAKE, t=FAKE, ws=FAKE, wsb=256):
+    return fos.lib().fos_quantize(ctypes.byref(c) if c is not None else None, x, rows, cols, rd, rs,
+                                  cd, cs, t, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,args,want", [
+    ({}, dict(cols=40), fos.FOS_E_SHAPE),
+    ({}, dict(rows=-1), fos.FOS_E_SHAPE),
+    (dict(outputs=("col",)), dict(rows=40), fos.FOS_E_SHAPE),
+    (dict(block="2d"), dict(rows=24), fos.FOS_E_SHAPE),
+    ({}, dict(x=None), fos.FOS_E_NULL),
+    ({}, dict(x=MIS), fos.FOS_E_ALIGN),
+    ({}, dict(rd=None), fos.FOS_E_NULL),
+    ({}, dict(rd=ctypes.c_void_p(0x100004)), fos.FOS_E_ALIGN),
+    (dict(outputs=("col",)), dict(cs=None), fos.FOS_E_NULL),
+    ({}, dict(t=None), fos.FOS_E_NULL),
+    ({}, dict(ws=None), fos.FOS_E_WORKSPACE),
+    ({}, dict(wsb=4), fos.FOS_E_WORKSPACE),
+    (dict(raw={"rule": 7}), {}, fos.FOS_E_FLAGS),
+    (dict(raw={"rounding": 2}), {}, fos.FOS_E_FLAGS),
+    (dict(raw={"outputs": 0}), {}, fos.FOS_E_FLAGS),
+    (dict(raw={"outputs": 4}), {}, fos.FOS_E_FLAGS),
+    (dict(raw={"struct_size": 8}), {}, fos.FOS_E_FLAGS),
+    (dict(block="2d", hadamard_seed=1), {}, fos.FOS_E_FLAGS),
+    (dict(outputs=("row", "col"), hadamard_seed=1), {}, fos.FOS_E_FLAGS),
+])
+def test_quantize_validation(kw, args, want):
+    assert q(cfg(**kw), **args) == want
+
+
+def test_quantize_null_config():
+    assert q(None) == fos.FOS_E_NULL
+
+
+def test_dequantize_validation():
+    L = fos.lib()
+    assert L.fos_dequantize(FAKE, FAKE, FAKE, 4, 40, 0, FAKE, None) == fos.FOS_E_SHAPE
+    assert L.fos_dequantize(FAKE, FAKE, FAKE, 4, 32, 5, FAKE, None) == fos.FOS_E_FLAGS
+    assert L.fos_dequantize(None, FAKE, FAKE, 4, 32, 0, FAKE, None) == fos.FOS_E_NULL
+    assert L.fos_dequantize(FAKE, FAKE, FAKE, 4, 32, 0, MIS, None) == fos.FOS_E_ALIGN
+    assert L.fos_dequantize(None, None, None, 0, 32, 0, None, None) == fos.FOS_OK   # empty
+
+
+def test_qlinear_validation():
+    L = fos.lib()
+    f = FAKE
+    assert L.fos_qlinear_fwd(f, f, f, f, f, f, 256, 256, 100, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_qlinear_fwd(f, f, f, f, f, f, 0, 256, 256, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_qlinear_fwd(f, f, f, f, f, f, 256, 256, 32, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_qlinear_fwd(None, f, f, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_NULL
+    assert L.fos_qlinear_fwd(MIS, f, f, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_ALIGN
+
+
+def test_tensor_scale_validation():
+    L = fos.lib()
+    c = cfg()
+    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 24, FAKE, FAKE, 256, None) == fos.FOS_E_SHAPE
+    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 32, None, FAKE, 256, None) == fos.FOS_E_NULL
+    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 32, FAKE, FAKE, 8, None) == fos.FOS_E_WORKSPACE
+    c2 = cfg(outputs=("col",), hadamard_seed=3)
+    assert L.fos_tensor_scale(ctypes.byref(c2), FAKE, 24, 32, FAKE, FAKE, 256, None) == fos.FOS_E_SHAPE

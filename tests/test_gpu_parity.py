@@ -1,0 +1,351 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: packed nibbles, scale bytes and the tensor scale bit-exact; dequantized fp32 and
+bf16 values bit-exact; qlinear within 1e-3 normwise of the bf16-rounded fp64
+reference (plus an element-wise bound from fp32 accumulation).  Oracle inputs are
+the seeded workloads or the oracle's own quantized bytes, never HIP outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp4_block_quantization_amd import workloads as W
+from oracle import formats as F
+from oracle import nvfp4 as N
+from oracle.qlinear import operand_exact, qlinear_ref64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def fos():
+    from fp4_block_quantization_amd import fos as mod
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return mod
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def to_gpu_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def gpu_quantize(fos, bits, cfg: N.Config, tensor_scale=None):
+    x = to_gpu_bf16(bits)
+    outs = [o for o, on in (("row", cfg.rows_out), ("col", cfg.cols_out)) if on]
+    res = fos.quantize(x, rule=cfg.rule, rounding=cfg.rounding, block=cfg.block, outputs=outs,
+                       hadamard_seed=cfg.hadamard_seed if cfg.hadamard else None,
+                       sr_seed=cfg.sr_seed if cfg.rounding == "sr" else None,
+                       tensor_scale=tensor_scale)
+    res = res if isinstance(res, tuple) else (res,)
+    torch.cuda.synchronize()
+    out = {"t": np.float32(res[0].tensor_scale.cpu().numpy()[0])}
+    for r in res:
+        out[f"{r.layout}_data"] = r.data.cpu().numpy()
+        out[f"{r.layout}_scales"] = r.scales.cpu().numpy()
+    return out
+
+
+def assert_same_bytes(got, want, what):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first {bad[:5].tolist()} " \
+                          f"got {got[tuple(bad[0])]:#x} want {want[tuple(bad[0])]:#x}"
+
+
+def assert_quant_equal(g, o):
+    assert g["t"].view(np.uint32) == np.float32(o["t"]).view(np.uint32), (g["t"], o["t"])
+    for k in ("row_data", "row_scales", "col_data", "col_scales"):
+        if k in o:
+            assert_same_bytes(g[k], o[k], k)
+
+
+# ------------------------------------------------------------------ small, all options
+
+CFGS = {
+    "row": N.Config(),
+    "row6": N.Config(rule="6"),
+    "row_sr": N.Config(rounding="sr", sr_seed=1234),
+    "row_rht": N.Config(hadamard=True, hadamard_seed=7),
+    "row_rht_sr": N.Config(hadamard=True, hadamard_seed=0, rounding="sr", sr_seed=99),
+    "col": N.Config(rows_out=False, cols_out=True),
+    "rowcol": N.Config(cols_out=True),
+    "rowcol6": N.Config(cols_out=True, rule="6"),
+    "rowcol_sr": N.Config(cols_out=True, rounding="sr", sr_seed=2 ** 40 + 3),
+    "col_rht": N.Config(rows_out=False, cols_out=True, hadamard=True, hadamard_seed=5),
+    "col_rht_sr": N.Config(rows_out=False, cols_out=True, hadamard=True, hadamard_seed=5,
+                           rounding="sr", sr_seed=8),
+    "2d": N.Config(block="2d"),
+    "2d6": N.Config(block="2d", rule="6"),
+    "2d_rowcol": N.Config(block="2d", cols_out=True),
+    "2d_col": N.Config(block="2d", rows_out=False, cols_out=True),
+    "2d_sr_rowcol": N.Config(block="2d", cols_out=True, rounding="sr", sr_seed=77),
+}
+SHAPES = [(16, 16), (48, 80), (272, 1040), (64, 4112), (528, 64)]
+DISTS = ["normal", "student_t", "uniform"]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("cfg_name", list(CFGS))
+def test_quantize_matches_oracle(fos, shape, cfg_name):
+    cfg = CFGS[cfg_name]
+    R, C = shape
+    for i, dist in enumerate(DISTS):
+        seed = 1000 * SHAPES.index(shape) + 10 * list(CFGS).index(cfg_name) + i
+        bits = bits_of(W.random_bf16(R, C, seed, dist, scale=0.05 * (i + 1), outlier_every=97,
+                                     outlier_mult=40.0))
+        o = N.quantize(bits, cfg)
+        g = gpu_quantize(fos, bits, cfg)
+        assert_quant_equal(g, o)
+
+
+@pytest.mark.parametrize("rows", [1, 3, 7])
+def test_row_wise_any_row_count(fos, rows):
+    bits = bits_of(W.random_bf16(rows, 4096 + 48, 55 + rows, "student_t"))
+    for cfg in (CFGS["row"], CFGS["row_sr"], CFGS["row_rht"]):
+        assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
+
+
+# ------------------------------------------------------------------ crafted cases
+
+def _all_bf16_up_to_six():
+    b = np.arange(0, 0x7F80, dtype=np.uint16)
+    v = F.bf16_bits_to_f32(b)
+    b = b[v <= 6.0]
+    return np.concatenate([b, b | np.uint16(0x8000)])
+
+
+@pytest.mark.parametrize("rule", ["6", "4/6"])
+def test_every_bf16_value_through_the_codec(fos, rule):
+    # Row 0 holds 2688 so t == 1; every other block is [6, x1..x15] so the 6-candidate
+    # scale is exactly 1 and v == x: the E2M1 rounding sees every bf16 magnitude <= 6
+    # (all round-to-nearest-even ties included) with both signs and signed zeros.
+    vals = _all_bf16_up_to_six()
+    pad = (-len(vals)) % 15
+    vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 15)
+    six = F.f32_to_bf16_bits(np.float32([6.0]))[0]
+    blocks = np.concatenate([np.full((len(vals), 1), six, np.uint16), vals], axis=1)
+    first = np.zeros((1, 16), np.uint16)
+    first[0, 0] = F.f32_to_bf16_bits(np.float32([2688.0]))[0]
+    rows = np.concatenate([first, blocks])
+    pad_rows = (-rows.shape[0]) % 16
+    rows = np.concatenate([rows, np.zeros((pad_rows, 16), np.uint16)])
+    bits = rows
+    cfg = N.Config(rule=rule)
+    o = N.quantize(bits, cfg)
+    assert o["t"] == np.float32(1.0)
+    assert_quant_equal(gpu_quantize(fos, bits, cfg), o)
+
+
+def test_ties_and_signed_zeros(fos):
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -2.5, -5.0, 0.0, -0.0, 1e-40, -1e-40]
+    x = np.zeros((32, 32), np.float32)
+    x[0, 0] = 2688.0
+    x[1, :16] = ties
+    x[2, :16] = np.array(ties) * 1.5
+    x[3, 16:] = -0.0
+    x[5, :] = 1e-3
+    bits = F.f32_to_bf16_bits(x)
+    bits[3, 16:] = np.uint16(0x8000)
+    for cfg in (N.Config(), N.Config(rule="6"), N.Config(cols_out=True), N.Config(block="2d", cols_out=True)):
+        assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
+
+
+@pytest.mark.parametrize("case", ["zeros", "neg_zeros", "single", "subnormal", "huge", "tiny_mixed"])
+def test_degenerate_tensors(fos, case):
+    R, C = 32, 64
+    x = np.zeros((R, C), np.float32)
+    if case == "single":
+        x[7, 20] = -3.25
+    elif case == "subnormal":
+        x[:] = np.random.default_rng(1).standard_normal((R, C)) * 1e-39
+    elif case == "huge":
+        x[:] = np.random.default_rng(2).standard_normal((R, C)) * 1e37
+    elif case == "tiny_mixed":
+        x[:] = np.random.default_rng(3).standard_normal((R, C)) * 1e-30
+        x[0, 0] = 1e-20
+    bits = F.f32_to_bf16_bits(x)
+    if case == "neg_zeros":
+        bits[:] = np.uint16(0x8000)
+    for cfg in (N.Config(cols_out=True), N.Config(block="2d"), N.Config(rounding="sr", sr_seed=3),
+                N.Config(hadamard=True, hadamard_seed=2)):
+        assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
+
+
+def test_empty_tensor(fos):
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    q = fos.quantize(x)
+    torch.cuda.synchronize()
+    assert q.data.shape == (0, 32) and float(q.tensor_scale.cpu()[0]) == 0.0
+
+
+def test_quantize_scaled_with_given_scale(fos):
+    bits = bits_of(W.random_bf16(64, 256, 5, "normal"))
+    cfg = N.Config(cols_out=True)
+    o = N.quantize(bits, cfg, t=np.float32(0.125))
+    t = torch.tensor([0.125], dtype=torch.float32, device=DEV)
+    assert_quant_equal(gpu_quantize(fos, bits, cfg, tensor_scale=t), o)
+
+
+def test_deterministic(fos):
+    bits = bits_of(W.random_bf16(512, 1024, 9, "student_t"))
+    for cfg in (CFGS["rowcol_sr"], CFGS["2d"], CFGS["row_rht_sr"]):
+        a, b = gpu_quantize(fos, bits, cfg), gpu_quantize(fos, bits, cfg)
+        for k in a:
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k]))
+
+
+# ------------------------------------------------------------------ dequantize
+
+@pytest.mark.parametrize("cfg_name", ["row", "row_sr", "col", "2d", "row6"])
+@pytest.mark.parametrize("shape", [(48, 80), (272, 1040)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_dequantize_matches_oracle(fos, cfg_name, shape):
+    cfg = CFGS[cfg_name]
+    bits = bits_of(W.random_bf16(*shape, 31, "student_t", outlier_every=53, outlier_mult=30.0))
+    o = N.quantize(bits, cfg)
+    lay = "row" if cfg.rows_out else "col"
+    data, scales = o[f"{lay}_data"], o[f"{lay}_scales"]
+    want = N.dequantize(data, scales, o["t"])
+    d = torch.from_numpy(data).to(DEV)
+    s = torch.from_numpy(scales).to(DEV)
+    t = torch.tensor([o["t"]], dtype=torch.float32, device=DEV)
+    q = fos.NVFP4Tensor(d, s, t, lay)
+    g32 = fos.dequantize(q, torch.float32).cpu().numpy()
+    g16 = bits_of(fos.dequantize(q, torch.bfloat16).cpu())
+    assert_same_bytes(g32.view(np.uint32), want.view(np.uint32), "fp32")
+    assert_same_bytes(g16, F.f32_to_bf16_bits(want), "bf16")
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.fixture(scope="module")
+def workloads():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache[name] = bits_of(W.make(name))
+        return cache[name]
+    return get
+
+
+def test_c1_full(fos, workloads):
+    bits = workloads("c1")
+    cfg = N.Config()
+    o = N.quantize(bits, cfg)
+    g = gpu_quantize(fos, bits, cfg)
+    assert_quant_equal(g, o)
+    d = torch.from_numpy(o["row_data"]).to(DEV)
+    s = torch.from_numpy(o["row_scales"]).to(DEV)
+    t = torch.tensor([o["t"]], dtype=torch.float32, device=DEV)
+    y = fos.dequantize(fos.NVFP4Tensor(d, s, t), torch.float32).cpu().numpy()
+    assert_same_bytes(y.view(np.uint32), N.dequantize(o["row_data"], o["row_scales"], o["t"]).view(np.uint32), "deq")
+
+
+def _sample_rows(R, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, R - 1], rng.choice(R, n, replace=False)]))
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("c2", N.Config()),
+    ("c4a", N.Config(hadamard=True, hadamard_seed=0, rounding="sr", sr_seed=1234)),
+])
+def test_full_size_row_wise_sampled(fos, workloads, name, cfg):
+    bits = workloads(name)
+    _, t = N.prepare(bits, cfg)
+    g = gpu_quantize(fos, bits, cfg)
+    assert g["t"].view(np.uint32) == t.view(np.uint32)
+    rows = _sample_rows(bits.shape[0], 96, 1)
+    o = N.quantize_rows_sampled(bits, cfg, t, rows)
+    assert_same_bytes(g["row_data"][rows], o["row_data"], "row_data")
+    assert_same_bytes(g["row_scales"][rows], o["row_scales"], "row_scales")
+
+
+def test_full_size_c3_row_and_col_sampled(fos, workloads):
+    bits = workloads("c3")
+    cfg = N.Config(cols_out=True)
+    _, t = N.prepare(bits, cfg)
+    g = gpu_quantize(fos, bits, cfg)
+    assert g["t"].view(np.uint32) == t.view(np.uint32)
+    rows = _sample_rows(bits.shape[0], 64, 2)
+    o = N.quantize_rows_sampled(bits, N.Config(), t, rows)
+    assert_same_bytes(g["row_data"][rows], o["row_data"], "row_data")
+    assert_same_bytes(g["row_scales"][rows], o["row_scales"], "row_scales")
+    cols = _sample_rows(bits.shape[1], 64, 3)
+    xt = np.ascontiguousarray(bits[:, cols].T)                 # columns as rows
+    oc = N.quantize_rows_sampled(xt, N.Config(), t, np.arange(len(cols)))
+    assert_same_bytes(g["col_data"][cols], oc["row_data"], "col_data")
+    assert_same_bytes(g["col_scales"][cols], oc["row_scales"], "col_scales")
+
+
+def test_full_size_c4b_2d_sampled(fos, workloads):
+    bits = workloads("c4b")
+    cfg = N.Config(block="2d")
+    _, t = N.prepare(bits, cfg)
+    g = gpu_quantize(fos, bits, cfg)
+    assert g["t"].view(np.uint32) == t.view(np.uint32)
+    for I in _sample_rows(bits.shape[0] // 16, 24, 4):
+        o = N.quantize(bits[16 * I:16 * I + 16], cfg, t=t)
+        assert_same_bytes(g["row_data"][16 * I:16 * I + 16], o["row_data"], f"tile-row {I}")
+        assert_same_bytes(g["row_scales"][16 * I:16 * I + 16], o["row_scales"], f"tile-row {I}")
+
+
+# ------------------------------------------------------------------ qlinear
+
+def _qlinear_check(y_gpu, xd, xs, xt, wd, ws, wt, rows=None, cols=None):
+    y64 = qlinear_ref64(xd, xs, xt, wd, ws, wt, rows, cols)
+    yg = F.bf16_bits_to_f32(y_gpu).astype(np.float64)
+    if rows is not None:
+        yg = yg[np.ix_(rows, cols)]
+    ref16 = F.bf16_bits_to_f32(F.f32_to_bf16_bits(y64.astype(np.float32))).astype(np.float64)
+    rel = np.linalg.norm(yg - ref16) / max(np.linalg.norm(y64), 1e-300)
+    assert rel <= 1e-3, rel
+    # element-wise: bf16 rounding + fp32 accumulation of exact products
+    ax = np.abs(operand_exact(xd, xs, rows))
+    bw = np.abs(operand_exact(wd, ws, cols))
+    K = ax.shape[1]
+    bound = 2.0 ** -8 * np.abs(y64) + 1.01 * K * 2.0 ** -24 * float(xt) * float(wt) * (ax @ bw.T) + 1e-30
+    assert np.all(np.abs(yg - y64) <= bound), np.max(np.abs(yg - y64) / bound)
+    return rel
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 64), (512, 768, 320), (200, 72, 128), (1, 16, 64),
+                                   (300, 520, 1024)])
+def test_qlinear_matches_fp64_reference(fos, m, n, k):
+    xb = bits_of(W.random_bf16(m, k, m + k, "student_t"))
+    wb = bits_of(W.random_bf16(n, k, n + 3 * k, "normal", scale=0.02))
+    ox, ow = N.quantize(xb, N.Config()), N.quantize(wb, N.Config())
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    tx = torch.tensor([ox["t"]], dtype=torch.float32, device=DEV)
+    tw = torch.tensor([ow["t"]], dtype=torch.float32, device=DEV)
+    xq = fos.NVFP4Tensor(dev(ox["row_data"]), dev(ox["row_scales"]), tx)
+    wq = fos.NVFP4Tensor(dev(ow["row_data"]), dev(ow["row_scales"]), tw)
+    y = bits_of(fos.qlinear_fwd(xq, wq).cpu())
+    _qlinear_check(y, ox["row_data"], ox["row_scales"], ox["t"], ow["row_data"], ow["row_scales"], ow["t"])
+
+
+def test_qlinear_full_size_c5_sampled(fos, workloads):
+    xb, wb = workloads("c5_x"), workloads("c5_w")
+    cfg = N.Config()
+    _, tx = N.prepare(xb, cfg)
+    _, tw = N.prepare(wb, cfg)
+    xq = fos.quantize(to_gpu_bf16(xb))
+    wq = fos.quantize(to_gpu_bf16(wb))
+    y = fos.qlinear_fwd(xq, wq)
+    torch.cuda.synchronize()
+    rows = _sample_rows(xb.shape[0], 62, 5)
+    cols = _sample_rows(wb.shape[0], 62, 6)
+    ox = N.quantize_rows_sampled(xb, cfg, tx, rows)
+    ow = N.quantize_rows_sampled(wb, cfg, tw, cols)
+    yb = bits_of(y.cpu())
+    # reference on the sampled rows / columns only
+    y64 = qlinear_ref64(ox["row_data"], ox["row_scales"], tx, ow["row_data"], ow["row_scales"], tw)
+    yg = F.bf16_bits_to_f32(yb[np.ix_(rows, cols)]).astype(np.float64)
+    ref16 = F.bf16_bits_to_f32(F.f32_to_bf16_bits(y64.astype(np.float32))).astype(np.float64)
+    rel = np.linalg.norm(yg - ref16) / np.linalg.norm(y64)
+    assert rel <= 1e-3, rel
