@@ -30,9 +30,10 @@ kept; "RN(.)" is one fp32 rounding):
         m_i  = E2M1 round-to-nearest-even of |v_i| (saturating at 6), or the
                stochastic rounding of O9;
         e_i  = RN(E(m_i) * d_c - |x_i|)            one rounding of the exact error
-        err_c = sum of RN(e_i * e_i) in fp32, i ascending (sequential, no FMA);
-               2D: per-row sequential partials, then the 16 row partials are summed
-               pairwise ((p0+p1)+(p2+p3))+... .
+        err_c: acc = 0; for i ascending acc = RN(e_i * e_i + acc) (fused
+               multiply-add, one rounding per step);
+               2D: one such accumulation per tile row, then the 16 row partials are
+               summed pairwise ((p0+p1)+(p2+p3))+... with plain fp32 additions.
   O6  choose 4 iff err_4 < err_6 (ties, including 0 == 0, go to 6).
   O7  nibble q_i = (sign bit of x_i) << 3 | m_i; byte k of a block holds q_2k in the
       low and q_2k+1 in the high nibble; scale byte S of the chosen candidate; 2D
@@ -50,7 +51,8 @@ kept; "RN(.)" is one fp32 rounding):
 
 The element-wise scale uses a per-block reciprocal and the per-block scale uses a
 per-tensor reciprocal (u_c); the error is the exact dequantization error rounded
-once.  These are readings: the pages fix none of these rounding steps.
+once and is accumulated with fused multiply-adds.  These are readings: the pages fix
+none of these rounding steps.
 """
 from __future__ import annotations
 
@@ -61,6 +63,7 @@ import numpy as np
 
 from .formats import (E2M1_GRID, bf16_bits_to_f32, e2m1_rne_code, e4m3_rne_sat,
                       e4m3_value)
+from .fparith import fma32
 from .hadamard import rht_blocks, rht_signs
 from .philox import philox4x32_10, split_seed
 
@@ -158,15 +161,14 @@ def _candidate(x: np.ndarray, a: np.ndarray, t: F32, c: float,
     emag = E2M1_GRID[m]
     dd = np.broadcast_to(d.reshape(shape_b), x.shape)
     e = _exact_error(emag, dd, np.abs(x))
-    sq = (e * e).astype(F32)
     if not two_d:
         acc = np.zeros(x.shape[0], dtype=F32)
         for i in range(16):
-            acc = (acc + sq[:, i]).astype(F32)
+            acc = fma32(e[:, i], e[:, i], acc)
         return S, m, acc
     rows = np.zeros(x.shape[:2], dtype=F32)                 # (n, 16) row partials
     for j in range(16):
-        rows = (rows + sq[:, :, j]).astype(F32)
+        rows = fma32(e[:, :, j], e[:, :, j], rows)
     level = rows
     while level.shape[1] > 1:                               # pairwise over rows
         level = (level[:, 0::2] + level[:, 1::2]).astype(F32)
