@@ -65,10 +65,18 @@ def time_loop(fn, steps, warmup, rotate):
     return s.elapsed_time(e) / steps
 
 
+def _vp(t):
+    import ctypes
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
 class QuantCase:
-    """Rotating input/output sets for one quantize configuration."""
+    """Rotating input/output sets for one quantize configuration.  The C ABI calls
+    are pre-marshalled (pointers, sizes, stream) so that the Python side issues each
+    call in about a microsecond and the GPU is never starved between launches."""
 
     def __init__(self, fos, x_cpu, cfg_kw, sets):
+        import ctypes
         import torch
         self.fos = fos
         self.cfg = fos.make_config(**cfg_kw)
@@ -89,17 +97,29 @@ class QuantCase:
         self.t = [torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(sets)]
         self.ws = fos.workspace(dev)
         self.sets = sets
+        lib = fos.lib()
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        cref = ctypes.byref(self.cfg)
+        nws = self.ws.numel()
+        self._q, self._qs, self._ts = lib.fos_quantize, lib.fos_quantize_scaled, lib.fos_tensor_scale
+        self.args_q, self.args_qs, self.args_ts = [], [], []
+        for i in range(sets):
+            rd, rs, cd, cs = self.out[i]
+            x, t = _vp(self.x[i]), _vp(self.t[i])
+            self.args_q.append((cref, x, R, C, _vp(rd), _vp(rs), _vp(cd), _vp(cs), t,
+                                _vp(self.ws), nws, stream))
+            self.args_qs.append((cref, x, R, C, t, _vp(rd), _vp(rs), _vp(cd), _vp(cs), stream))
+            self.args_ts.append((cref, x, R, C, t, _vp(self.ws), nws, stream))
+        self.bad = 0
 
     def step(self, i):
-        rd, rs, cd, cs = self.out[i]
-        self.fos.fos_quantize(self.cfg, self.x[i], rd, rs, cd, cs, self.t[i], self.ws)
+        self.bad |= self._q(*self.args_q[i])
 
     def scaled(self, i):
-        rd, rs, cd, cs = self.out[i]
-        self.fos.fos_quantize_scaled(self.cfg, self.x[i], self.t[i], rd, rs, cd, cs)
+        self.bad |= self._qs(*self.args_qs[i])
 
     def scale_only(self, i):
-        self.fos.fos_tensor_scale(self.cfg, self.x[i], self.t[i], self.ws)
+        self.bad |= self._ts(*self.args_ts[i])
 
 
 def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1):
@@ -109,6 +129,8 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1):
     ms = time_loop(case.step, steps, warmup, sets)
     ms_k = time_loop(case.scaled, steps, warmup, sets)
     ms_a = time_loop(case.scale_only, steps, warmup, sets)
+    if case.bad:
+        raise RuntimeError(f"{name}: a fos call returned an error status")
     b = quant_bytes(R, C, n_out)
     row = {"workload": name, "shape": [R, C], "options": {k: (list(v) if isinstance(v, tuple) else v)
                                                           for k, v in cfg_kw.items()},
@@ -122,20 +144,30 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1):
 
 
 def bench_dequant(fos, x_cpu, steps, warmup):
+    import ctypes
     import torch
     R, C = x_cpu.shape
     dev = "cuda:0"
     q = fos.quantize(x_cpu.to(dev))
+    lib = fos.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     rows = {}
-    for dt, name, ob in ((torch.bfloat16, "bf16", 2), (torch.float32, "f32", 4)):
+    for dt, name, ob, code in ((torch.bfloat16, "bf16", 2, fos.FOS_OUT_BF16),
+                               (torch.float32, "f32", 4, fos.FOS_OUT_F32)):
         sets = 3
         outs = [torch.empty(R, C, dtype=dt, device=dev) for _ in range(sets)]
         datas = [q.data.clone() for _ in range(sets)]
         scs = [q.scales.clone() for _ in range(sets)]
+        args = [(_vp(datas[i]), _vp(scs[i]), _vp(q.tensor_scale), R, C, code, _vp(outs[i]), stream)
+                for i in range(sets)]
+        f = lib.fos_dequantize
+        bad = [0]
 
         def fn(i):
-            fos.fos_dequantize(datas[i], scs[i], q.tensor_scale, R, C, outs[i])
+            bad[0] |= f(*args[i])
         ms = time_loop(fn, steps, warmup, sets)
+        if bad[0]:
+            raise RuntimeError("fos_dequantize returned an error status")
         b = R * C // 2 + R * C // 16 + 4 + ob * R * C
         rows[name] = {"bytes": b, "ms": ms, "GBps": b / ms / 1e6, "frac": b / ms / 1e6 / HBM_PEAK_GBS}
         del outs
@@ -158,6 +190,19 @@ def bench_qlinear(fos, x_cpu, w_cpu, steps, warmup):
     flops = 2 * M * N * K
     return {"shape": [M, N, K], "flop": flops, "ms": ms, "TFLOPs": flops / ms / 1e9,
             "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+
+
+def copy_reference(steps):
+    """A plain device-to-device copy (torch's copy kernel) of 256 MiB: a measured
+    ceiling for streaming read+write traffic on this GPU."""
+    import torch
+    n = 256 * 2 ** 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
+
+    def fn(i):
+        bufs[2 * (i % 2) + 1].copy_(bufs[2 * (i % 2)])
+    ms = time_loop(fn, steps, 3, 2)
+    return {"bytes": 2 * n, "ms": ms, "GBps": 2 * n / ms / 1e6, "frac": 2 * n / ms / 1e6 / HBM_PEAK_GBS}
 
 
 def cpu_baseline(x_cpu, rows_sample):
@@ -244,6 +289,8 @@ def main():
     log("C4b ...")
     rows["c4b_2d"] = bench_quant(fos, "c4b weight 12288x4096, 2D 16x16", W.make("c4b"),
                                  {"block": "2d"}, args.steps, args.warmup)
+    log("copy reference ...")
+    rows["hbm_copy_reference"] = copy_reference(args.steps)
     log("C5 qlinear ...")
     rows["c5_qlinear"] = bench_qlinear(fos, W.make("c5_x"), W.make("c5_w"), args.steps, args.warmup)
     log(json.dumps(rows["c5_qlinear"]))

@@ -1,12 +1,12 @@
 // Per-tensor scale: t = max|x| / 2688 (one FP32 scale per tensor, Ultralytics
 // glossary "FP4", section "How FP4 works"; 2688 = 448 * 6).
 //
-// One pass over the tensor.  Each thread folds |x| into a running maximum (integer
-// max of bf16 bit patterns with the sign cleared: for non-negative floats the bit
-// order is the value order), the wave reduces with lane shuffles, the workgroup
-// through LDS, and one u32 atomic max per workgroup merges into the workspace cell.
-// The last workgroup to finish (counted with a second atomic) turns the maximum
-// into t and clears both workspace words for the next call.
+// One streaming pass writes one partial maximum per workgroup into the caller's
+// workspace (plain stores: no atomics, no fences, nothing to clear between calls);
+// a one-workgroup kernel then reduces the partials and writes t.  Each thread folds
+// |x| into a running maximum (integer max of bf16 bit patterns with the sign cleared:
+// for non-negative floats the bit order is the value order); the wave reduces with
+// lane shuffles and the workgroup through LDS.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -31,55 +31,37 @@ __device__ __forceinline__ uint32_t pk_max_abs4(uint32_t m, const uint4& w) {
   return pk_max_abs(m, w.w);
 }
 
-// Block-wide max of `bits` (fp32 patterns of non-negative values), atomic merge into
-// ws[0], and last-block finalisation of t.
-__device__ __forceinline__ void reduce_and_finalize(uint32_t bits, uint32_t* ws, float* tscale) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) bits = max(bits, (uint32_t)__shfl_xor((int)bits, off));
-  __shared__ uint32_t part[kThreads / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) part[wave] = bits;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = part[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) m = max(m, part[w]);
-    atomicMax(&ws[0], m);
-    __threadfence();
-    const uint32_t prev = atomicAdd(&ws[1], 1u);
-    if (prev == gridDim.x - 1) {
-      __threadfence();
-      const uint32_t a = atomicOr(&ws[0], 0u);
-      tscale[0] = __uint_as_float(a) / kScaleDenom;
-      atomicExch(&ws[0], 0u);
-      atomicExch(&ws[1], 0u);
-    }
-  }
+// Block-wide max of `bits` (fp32 patterns of non-negative values) -> partials[block].
+__device__ __forceinline__ void write_partial(uint32_t bits, float* partials) {
+  bits = block_max_u32(bits);
+  if (threadIdx.x == 0) partials[blockIdx.x] = __uint_as_float(bits);
 }
 
-// No transform: flat pass over 16-byte chunks (8 bf16).
+// No transform: flat pass over 16-byte chunks (8 bf16); eight independent 16-byte
+// loads per lane are issued before any is consumed (128 KB in flight per CU at four
+// workgroups per CU).
+constexpr int kUnroll = 8;
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const uint4* __restrict__ x,
-                                                             int64_t n16, uint32_t* ws,
-                                                             float* tscale) {
+                                                             int64_t n16, float* partials) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   uint32_t m = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 w0 = x[i], w1 = x[i + stride], w2 = x[i + 2 * stride], w3 = x[i + 3 * stride];
-    m = pk_max_abs4(m, w0);
-    m = pk_max_abs4(m, w1);
-    m = pk_max_abs4(m, w2);
-    m = pk_max_abs4(m, w3);
+  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    uint4 w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) w[u] = x[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) m = pk_max_abs4(m, w[u]);
   }
   for (; i < n16; i += stride) m = pk_max_abs4(m, x[i]);
   const uint32_t bits = max(m & 0xffffu, m >> 16) << 16;
-  reduce_and_finalize(bits, ws, tscale);
+  write_partial(bits, partials);
 }
 
 // Hadamard along rows: every 16-value block (two 16-byte chunks) is transformed.
 __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const uint4* __restrict__ x,
                                                                  int64_t nblk, uint32_t mask,
-                                                                 uint32_t* ws, float* tscale) {
+                                                                 float* partials) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   float m = 0.0f;
   for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
@@ -89,15 +71,14 @@ __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const uint4* __
     rht16(v, mask);
     m = fmaxf(m, amax16(v));
   }
-  reduce_and_finalize(__float_as_uint(m), ws, tscale);
+  write_partial(__float_as_uint(m), partials);
 }
 
 // Hadamard along columns: a thread owns a patch of 16 rows x 8 columns and
 // transforms each of its 8 column blocks.
 __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const uint16_t* __restrict__ x,
                                                                  int64_t rows, int64_t cols,
-                                                                 uint32_t mask, uint32_t* ws,
-                                                                 float* tscale) {
+                                                                 uint32_t mask, float* partials) {
   const int64_t ncg = cols / 8;
   const int64_t npatch = (rows / 16) * ncg;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -119,34 +100,44 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const uint16_t*
       m = fmaxf(m, amax16(v));
     }
   }
-  reduce_and_finalize(__float_as_uint(m), ws, tscale);
+  write_partial(__float_as_uint(m), partials);
+}
+
+// Reduce the partials of the tensor-scale pass and write t.
+__global__ __launch_bounds__(kThreads) void scale_finalize_kernel(const float* __restrict__ partials,
+                                                                  int n, float* tscale) {
+  const float a = reduce_partials(partials, n);
+  if (threadIdx.x == 0) tscale[0] = a / kScaleDenom;
 }
 
 int grid_for(int64_t work_items, int per_thread) {
   int64_t g = (work_items + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
   if (g < 1) g = 1;
-  if (g > 4096) g = 4096;
+  if (g > kMaxPartials) g = kMaxPartials;
   return (int)g;
 }
 
 }  // namespace
 
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bool hadamard,
-                               bool hadamard_cols, uint32_t rht_mask, uint32_t* ws,
+                               bool hadamard_cols, uint32_t rht_mask, float* partials,
                                float* tscale, hipStream_t stream) {
   const int64_t n = rows * cols;
+  int g;
   if (!hadamard) {
     const int64_t n16 = n / 8;
-    amax_flat_kernel<<<grid_for(n16, 4), kThreads, 0, stream>>>((const uint4*)x, n16, ws, tscale);
+    g = grid_for(n16, kUnroll);
+    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n16, partials);
   } else if (!hadamard_cols) {
     const int64_t nblk = n / 16;
-    amax_rht_rows_kernel<<<grid_for(nblk, 2), kThreads, 0, stream>>>((const uint4*)x, nblk,
-                                                                     rht_mask, ws, tscale);
+    g = grid_for(nblk, 2);
+    amax_rht_rows_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, nblk, rht_mask, partials);
   } else {
     const int64_t npatch = (rows / 16) * (cols / 8);
-    amax_rht_cols_kernel<<<grid_for(npatch, 1), kThreads, 0, stream>>>(x, rows, cols, rht_mask,
-                                                                       ws, tscale);
+    g = grid_for(npatch, 1);
+    amax_rht_cols_kernel<<<g, kThreads, 0, stream>>>(x, rows, cols, rht_mask, partials);
   }
+  scale_finalize_kernel<<<1, kThreads, 0, stream>>>(partials, g, tscale);
   return hipGetLastError();
 }
 

@@ -4,11 +4,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace {
 
-constexpr size_t kWorkspaceBytes = 256;
+constexpr size_t kWorkspaceBytes = sizeof(float) * fos::kMaxPartials;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
@@ -105,13 +106,14 @@ fos::QuantArgs make_args(const fos_quant_config* cfg, const void* x, int64_t row
   return a;
 }
 
+// Tensor-scale pass (partial maxima in the workspace, then t into *tscale).
 fos_status launch_scale(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols,
                         float* tscale, void* ws, hipStream_t s) {
   const bool had = cfg->hadamard != 0;
   const uint32_t mask = had ? hadamard_mask(cfg->hadamard_seed) : 0u;
   const hipError_t e = fos::launch_tensor_scale(static_cast<const uint16_t*>(x), rows, cols, had,
                                                 had && wants_cols(cfg), mask,
-                                                static_cast<uint32_t*>(ws), tscale, s);
+                                                static_cast<float*>(ws), tscale, s);
   return e == hipSuccess ? FOS_OK : FOS_E_HIP;
 }
 
@@ -205,6 +207,9 @@ fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
   if (M < 1 || N < 1 || K < 64 || K % 64 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
     return FOS_E_SHAPE;
   if (N > kMaxElems / M || K > kMaxElems / M || K > kMaxElems / N) return FOS_E_SHAPE;
+  // each packed operand is addressed through one buffer resource (< 4 GiB)
+  if ((M + 256) * (K / 2) >= ((int64_t)1 << 32) || (N + 256) * (K / 2) >= ((int64_t)1 << 32))
+    return FOS_E_SHAPE;
   if (!x_data || !x_scales || !x_tensor_scale || !w_data || !w_scales || !w_tensor_scale ||
       !y_bf16)
     return FOS_E_NULL;

@@ -2,8 +2,12 @@
 // rounded once to fp32 (Ultralytics glossary "FP4", section "How FP4 works": the
 // dequantized value is the grid value times its sign times the block scale; the
 // NVFP4 block scale is itself an E4M3 number under a per-tensor FP32 scale).
-// One lane per 16-value block: an 8-byte nibble load, one scale byte, hardware
-// E2M1->fp32 conversion, and 64 (fp32) or 32 (bf16) output bytes.
+//
+// Output-major: lane g writes the g-th 16-byte chunk of the output (4 fp32 or 8 bf16
+// values), so every store instruction of a wave covers 1 KB of contiguous memory; it
+// reads the 2 or 4 nibble bytes of its chunk (contiguous across lanes) and the block's
+// scale byte (shared by the 4 or 2 lanes of a block).  Hardware E2M1 -> fp32
+// conversion; bf16 output rounds the fp32 value to nearest-even.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -12,42 +16,46 @@ namespace fos {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
 
 template <bool kBF16>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint2* __restrict__ data,
+__device__ __forceinline__ void dequant_chunk(const uint8_t* __restrict__ data,
+                                              const uint8_t* __restrict__ scales, float t,
+                                              int64_t g, void* __restrict__ out) {
+  if (kBF16) {
+    // 8 values = one 4-byte word of nibbles; block g/2
+    const uint32_t q = reinterpret_cast<const uint32_t*>(data)[g];
+    const float d = e4m3_decode(scales[g >> 1]) * t;
+    const f32x2 e0 = cvt_pk_f32_fp4<0>(q), e1 = cvt_pk_f32_fp4<1>(q);
+    const f32x2 e2 = cvt_pk_f32_fp4<2>(q), e3 = cvt_pk_f32_fp4<3>(q);
+    uint4 o;
+    o.x = f32_to_bf16_rne(e0.x * d) | (f32_to_bf16_rne(e0.y * d) << 16);
+    o.y = f32_to_bf16_rne(e1.x * d) | (f32_to_bf16_rne(e1.y * d) << 16);
+    o.z = f32_to_bf16_rne(e2.x * d) | (f32_to_bf16_rne(e2.y * d) << 16);
+    o.w = f32_to_bf16_rne(e3.x * d) | (f32_to_bf16_rne(e3.y * d) << 16);
+    reinterpret_cast<uint4*>(out)[g] = o;
+  } else {
+    // 4 values = one 2-byte half-word of nibbles; block g/4
+    const uint32_t q = reinterpret_cast<const uint16_t*>(data)[g];
+    const float d = e4m3_decode(scales[g >> 2]) * t;
+    const f32x2 e0 = cvt_pk_f32_fp4<0>(q), e1 = cvt_pk_f32_fp4<1>(q);
+    reinterpret_cast<float4*>(out)[g] = make_float4(e0.x * d, e0.y * d, e1.x * d, e1.y * d);
+  }
+}
+
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ tscale,
-                                                           int64_t nblk, void* __restrict__ out) {
+                                                           int64_t nchunk, void* __restrict__ out) {
   const float t = tscale[0];
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    const uint2 q = data[b];
-    const float d = e4m3_decode(scales[b]) * t;
-    f32x2 e[8];
-    e[0] = cvt_pk_f32_fp4<0>(q.x); e[1] = cvt_pk_f32_fp4<1>(q.x);
-    e[2] = cvt_pk_f32_fp4<2>(q.x); e[3] = cvt_pk_f32_fp4<3>(q.x);
-    e[4] = cvt_pk_f32_fp4<0>(q.y); e[5] = cvt_pk_f32_fp4<1>(q.y);
-    e[6] = cvt_pk_f32_fp4<2>(q.y); e[7] = cvt_pk_f32_fp4<3>(q.y);
-    float y[16];
+  int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; g + (kUnroll - 1) * stride < nchunk; g += kUnroll * stride) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      y[2 * j] = e[j].x * d;
-      y[2 * j + 1] = e[j].y * d;
-    }
-    if (kBF16) {
-      uint32_t w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        w[j] = f32_to_bf16_rne(y[2 * j]) | (f32_to_bf16_rne(y[2 * j + 1]) << 16);
-      uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
-      o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    } else {
-      float4* o = reinterpret_cast<float4*>(out) + 4 * b;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
-    }
+    for (int u = 0; u < kUnroll; ++u) dequant_chunk<kBF16>(data, scales, t, g + u * stride, out);
   }
+  for (; g < nchunk; g += stride) dequant_chunk<kBF16>(data, scales, t, g, out);
 }
 
 }  // namespace
@@ -55,16 +63,16 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint2* __restri
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
                              int64_t rows, int64_t cols, bool bf16_out, void* out,
                              hipStream_t s) {
-  const int64_t nblk = rows * cols / 16;
-  if (nblk == 0) return hipSuccess;
-  int64_t grid = (nblk + kThreads - 1) / kThreads;
-  if (grid > (int64_t)1 << 30) grid = (int64_t)1 << 30;
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  const int64_t nchunk = bf16_out ? n / 8 : n / 4;
+  int64_t grid = (nchunk + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
   if (bf16_out)
-    dequant_kernel<true><<<grid, kThreads, 0, s>>>(reinterpret_cast<const uint2*>(data), scales,
-                                                   tscale, nblk, out);
+    dequant_kernel<true><<<grid, kThreads, 0, s>>>(data, scales, tscale, nchunk, out);
   else
-    dequant_kernel<false><<<grid, kThreads, 0, s>>>(reinterpret_cast<const uint2*>(data), scales,
-                                                    tscale, nblk, out);
+    dequant_kernel<false><<<grid, kThreads, 0, s>>>(data, scales, tscale, nchunk, out);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@
 //   v_i = x_i * inv, code = E2M1 RNE(v_i) (hardware cvt, saturating at 6) or the
 //         stochastic rounding below
 //   e_i = fma(E(code_i), d, -x_i) (the exact error rounded once)
-//   err = sum_i e_i*e_i, sequential in i (2D: rows sequential, then pairwise)
+//   err = fma(e_i, e_i, err) for i ascending (2D: per row, then rows pairwise)
 // and the block keeps candidate 4 iff err_4 < err_6.
 #pragma once
 
@@ -28,6 +28,28 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kScaleDenom = 2688.0f;  // largest E4M3 (448) * largest E2M1 (6)
 constexpr float kMinNormal = 0x1p-126f;
+constexpr int kMaxPartials = 4096;      // workgroups of the tensor-scale pass
+
+// ---- workgroup reductions (every thread of the workgroup must call these) ---------
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  __shared__ uint32_t part[16];
+  const int nw = (blockDim.x + 63) >> 6;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t m = part[0];
+  for (int w = 1; w < nw; ++w) m = max(m, part[w]);
+  __syncthreads();
+  return m;
+}
+
+// Maximum of n non-negative partial maxima written by the tensor-scale pass.
+__device__ __forceinline__ float reduce_partials(const float* __restrict__ p, int n) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = max(m, __float_as_uint(p[i]));
+  return __uint_as_float(block_max_u32(m));
+}
 
 // ---- bf16 ----------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -181,9 +203,9 @@ __device__ __forceinline__ void cand_codes_rne(const float (&x)[16], float d, fl
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float e0 = __builtin_fmaf(e[j].x, d, -x[2 * j]);
-    err = err + e0 * e0;
+    err = __builtin_fmaf(e0, e0, err);
     const float e1 = __builtin_fmaf(e[j].y, d, -x[2 * j + 1]);
-    err = err + e1 * e1;
+    err = __builtin_fmaf(e1, e1, err);
   }
   c.lo = lo;
   c.hi = hi;
@@ -203,23 +225,19 @@ __device__ __forceinline__ void cand_codes_sr(const float (&x)[16], float d, flo
     const uint32_t q = m | ((__float_as_uint(x[i]) >> 28) & 8u);
     if (i < 8) lo |= q << (4 * i); else hi |= q << (4 * (i - 8));
     const float e = __builtin_fmaf(g, d, -fabsf(x[i]));
-    err = err + e * e;
+    err = __builtin_fmaf(e, e, err);
   }
   c.lo = lo;
   c.hi = hi;
   c.err = err;
 }
 
-// Per-lane 16-value block amax.
+// Per-lane 16-value block amax (a chain of 3-input maxima with |.| modifiers).
 __device__ __forceinline__ float amax16(const float (&x)[16]) {
-  float m0 = fmaxf(fabsf(x[0]), fabsf(x[1]));
-  float m1 = fmaxf(fabsf(x[2]), fabsf(x[3]));
+  float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2]));
 #pragma unroll
-  for (int i = 4; i < 16; i += 4) {
-    m0 = fmaxf(m0, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
-    m1 = fmaxf(m1, fmaxf(fabsf(x[i + 2]), fabsf(x[i + 3])));
-  }
-  return fmaxf(m0, m1);
+  for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, fabsf(x[i])), fabsf(x[i + 1]));
+  return fmaxf(m, fabsf(x[15]));
 }
 
 // Quantize one 1D block with both candidates (or 6 alone) and return the winner.

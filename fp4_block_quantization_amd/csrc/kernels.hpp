@@ -23,9 +23,10 @@ struct QuantArgs {
   bool hadamard;
 };
 
-// t = max|x| / 2688 into *tscale; ws = 2 zero-filled u32 (max cell, counter).
+// Tensor-scale pass: one partial max|x| per workgroup into `partials` (at most
+// kMaxPartials), then a one-workgroup kernel writes t = max / 2688 to *tscale.
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bool hadamard,
-                               bool hadamard_cols, uint32_t rht_mask, uint32_t* ws,
+                               bool hadamard_cols, uint32_t rht_mask, float* partials,
                                float* tscale, hipStream_t stream);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

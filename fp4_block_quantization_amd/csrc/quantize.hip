@@ -28,9 +28,10 @@ struct TensorConsts {
   float t, u6, u4;
 };
 
-__device__ __forceinline__ TensorConsts tensor_consts(const float* tscale) {
+// t from the caller's device scalar (written by the tensor-scale pass).
+__device__ __forceinline__ TensorConsts tensor_consts(const QuantArgs& a) {
   TensorConsts c;
-  c.t = tscale[0];
+  c.t = a.tscale[0];
   c.u6 = 1.0f / (c.t * 6.0f);
   c.u4 = 1.0f / (c.t * 4.0f);
   return c;
@@ -43,15 +44,32 @@ __device__ __forceinline__ void store_block(uint8_t* data, uint8_t* scales, int6
 }
 
 // ------------------------------------------------------------------ row-wise, 1D
+// Each lane owns blocks b and b + 256 of its workgroup's 512; both blocks' four
+// 16-byte loads are issued before either is quantized.
+constexpr int kRowsPerWG = 2 * kThreads;
+
 template <bool k46, bool kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
-  const TensorConsts tc = tensor_consts(a.tscale);
+  const TensorConsts tc = tensor_consts(a);
   const uint4* __restrict__ x = reinterpret_cast<const uint4*>(a.x);
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    const uint4 w0 = x[2 * b], w1 = x[2 * b + 1];
+  const int64_t b0 = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
+  uint4 w[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t b = b0 + q * kThreads;
+    w[2 * q] = make_uint4(0, 0, 0, 0);
+    w[2 * q + 1] = w[2 * q];
+    if (b < nblk) {
+      w[2 * q] = x[2 * b];
+      w[2 * q + 1] = x[2 * b + 1];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t b = b0 + q * kThreads;
+    if (b >= nblk) break;
     float v[16];
-    unpack16(w0, w1, v);
+    unpack16(w[2 * q], w[2 * q + 1], v);
     if (kRHT) rht16(v, a.rht_mask);
     float kk[16];
     if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, kk);
@@ -73,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
   const int64_t R0 = (int64_t)(blockIdx.x / tiles_c) * kTileR;
   const int64_t C0 = (int64_t)(blockIdx.x % tiles_c) * kTileC;
   const int tid = threadIdx.x;
-  const TensorConsts tc = tensor_consts(a.tscale);
+  const TensorConsts tc = tensor_consts(a);
 
   const int j = tid & 3;
 #pragma unroll
@@ -143,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   const int row = tid & 15, tl = tid >> 4;
   const int64_t T = (int64_t)(blockIdx.x % wg_per_row) * 16 + tl;
   const bool valid = T < tiles_c;
-  const TensorConsts tc = tensor_consts(a.tscale);
+  const TensorConsts tc = tensor_consts(a);
 
   float v[16];
   if (valid) {
@@ -214,8 +232,7 @@ template <bool k46, bool kSR, bool kRHT>
 hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
   if (!a.cols_out) {
     const int64_t nblk = a.rows * a.cols / 16;
-    int64_t grid = (nblk + kThreads - 1) / kThreads;
-    if (grid > (int64_t)1 << 30) grid = (int64_t)1 << 30;
+    const int64_t grid = (nblk + kRowsPerWG - 1) / kRowsPerWG;
     quant_rows_kernel<k46, kSR, kRHT><<<grid, kThreads, 0, s>>>(a, nblk);
     return hipGetLastError();
   }

@@ -20,7 +20,8 @@
  *   - Tensors are row-major and contiguous.  Element (r, c) of a [rows, cols] bf16
  *     tensor is at byte offset 2*(r*cols + c).
  *   - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
- *   - Calls are thread-safe; concurrent calls must not share a workspace.
+ *   - Calls are thread-safe; calls that may run concurrently (different streams)
+ *     must not share a workspace.
  *
  * NVFP4 record layout (one orientation):
  *   data   [R][C/2] bytes: byte k of a row holds element 2k in its low nibble and
@@ -94,9 +95,9 @@ int fos_abi_version(void);
 /* Human-readable name of a status (static string, never NULL). */
 const char* fos_status_string(fos_status status);
 
-/* Bytes of device workspace that fos_tensor_scale / fos_quantize need.  The caller
- * zero-fills the workspace once before its first use (e.g. hipMemset); every
- * successful call leaves it zero-filled again. */
+/* Bytes of device workspace that fos_tensor_scale / fos_quantize need (scratch for
+ * the per-workgroup partial maxima of the tensor-scale pass; its contents on entry
+ * are ignored, and it must stay untouched until the call's kernels have run). */
 size_t fos_workspace_bytes(void);
 
 /* Per-tensor scale.  Writes t = RN_fp32(A / 2688) to *tensor_scale (device fp32),
@@ -152,9 +153,10 @@ fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales,
  * [M][K/2], x_scales [M][K/16]) and Wq [N][K] (the [out][in] Linear layout).
  * E*D products are formed exactly in fp16, multiplied on the matrix cores with fp32
  * accumulation; the tensor scales are applied in fp32 before the bf16 rounding.
- *   M, N >= 1; K >= 64 and K % 64 == 0.  x_data, w_data 16-byte aligned;
- *   y_bf16 [M][N], 4-byte aligned with N even... any N is accepted: y is written
- *   with 2-byte stores at the edges.
+ *   M, N >= 1; K >= 64 and K % 64 == 0; (M + 256) * K / 2 and (N + 256) * K / 2
+ *   below 2^32 (each packed operand is one buffer resource).  x_data, w_data
+ *   16-byte aligned, x_scales, w_scales 4-byte aligned, y_bf16 [M][N] 2-byte
+ *   aligned.
  * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_HIP. */
 fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
                            const float* x_tensor_scale, const uint8_t* w_data,

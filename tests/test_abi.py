@@ -48,7 +48,8 @@ def cfg(**kw):
     return c
 
 
-def q(c, x=FAKE, rows=64, cols=64, rd=FAKE, rs=FAKE, cd=FAKE, cs=FAKE, t=FAKE, ws=FAKE, wsb=256):
+def q(c, x=FAKE, rows=64, cols=64, rd=FAKE, rs=FAKE, cd=FAKE, cs=FAKE, t=FAKE, ws=FAKE, wsb=None):
+    wsb = fos.lib().fos_workspace_bytes() if wsb is None else wsb
     return fos.lib().fos_quantize(ctypes.byref(c) if c is not None else None, x, rows, cols, rd, rs,
                                   cd, cs, t, ws, wsb, None)
 
@@ -99,13 +100,15 @@ def test_qlinear_validation():
     assert L.fos_qlinear_fwd(f, f, f, f, f, f, 256, 256, 32, f, None) == fos.FOS_E_SHAPE
     assert L.fos_qlinear_fwd(None, f, f, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_NULL
     assert L.fos_qlinear_fwd(MIS, f, f, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_ALIGN
+    # a packed operand must fit one buffer resource (< 4 GiB)
+    assert L.fos_qlinear_fwd(f, f, f, f, f, f, 1 << 20, 256, 1 << 13, f, None) == fos.FOS_E_SHAPE
 
 
 def test_tensor_scale_validation():
     L = fos.lib()
     c = cfg()
-    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 24, FAKE, FAKE, 256, None) == fos.FOS_E_SHAPE
-    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 32, None, FAKE, 256, None) == fos.FOS_E_NULL
+    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 24, FAKE, FAKE, 1 << 14, None) == fos.FOS_E_SHAPE
+    assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 32, None, FAKE, 4096, None) == fos.FOS_E_NULL
     assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 32, FAKE, FAKE, 8, None) == fos.FOS_E_WORKSPACE
     c2 = cfg(outputs=("col",), hadamard_seed=3)
-    assert L.fos_tensor_scale(ctypes.byref(c2), FAKE, 24, 32, FAKE, FAKE, 256, None) == fos.FOS_E_SHAPE
+    assert L.fos_tensor_scale(ctypes.byref(c2), FAKE, 24, 32, FAKE, FAKE, 1 << 14, None) == fos.FOS_E_SHAPE

@@ -315,7 +315,8 @@ def _qlinear_check(y_gpu, xd, xs, xt, wd, ws, wt, rows=None, cols=None):
 
 
 @pytest.mark.parametrize("m,n,k", [(256, 256, 64), (512, 768, 320), (200, 72, 128), (1, 16, 64),
-                                   (300, 520, 1024)])
+                                   (300, 520, 1024), (264, 136, 768), (512, 512, 256),
+                                   (1024, 768, 2048)])
 def test_qlinear_matches_fp64_reference(fos, m, n, k):
     xb = bits_of(W.random_bf16(m, k, m + k, "student_t"))
     wb = bits_of(W.random_bf16(n, k, n + 3 * k, "normal", scale=0.02))
