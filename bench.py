@@ -241,8 +241,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "layout is described in DESIGN.md and not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the multi-GPU "
+              "path (per-shard tensor scale, one 4-byte max all-reduce) is not built.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -37,23 +37,27 @@ __device__ __forceinline__ void write_partial(uint32_t bits, float* partials) {
   if (threadIdx.x == 0) partials[blockIdx.x] = __uint_as_float(bits);
 }
 
-// No transform: flat pass over 16-byte chunks (8 bf16); eight independent 16-byte
-// loads per lane are issued before any is consumed (128 KB in flight per CU at four
-// workgroups per CU).
-constexpr int kUnroll = 8;
+// No transform: each workgroup reduces one contiguous slab of 16-byte chunks (8
+// bf16), a multiple of 1024 chunks long; every lane issues four independent 16-byte
+// loads per iteration before consuming any.
+constexpr int kUnroll = 4;
+constexpr int64_t kSlabQuantum = (int64_t)kThreads * kUnroll;
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const uint4* __restrict__ x,
-                                                             int64_t n16, float* partials) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+                                                             int64_t n16, int64_t per,
+                                                             float* partials) {
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  const int64_t end = min(beg + per, n16);
   uint32_t m = 0;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+  for (int64_t i = beg + threadIdx.x; i < end; i += kSlabQuantum) {
     uint4 w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = x[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = i + u * kThreads;
+      w[u] = j < end ? x[j] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) m = pk_max_abs4(m, w[u]);
   }
-  for (; i < n16; i += stride) m = pk_max_abs4(m, x[i]);
   const uint32_t bits = max(m & 0xffffu, m >> 16) << 16;
   write_partial(bits, partials);
 }
@@ -103,10 +107,20 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const uint16_t*
   write_partial(__float_as_uint(m), partials);
 }
 
-// Reduce the partials of the tensor-scale pass and write t.
+// Reduce the partials of the tensor-scale pass and write t.  Every thread issues its
+// loads (n <= 4096 = 16 per thread; indices past n re-read the last partial, which
+// leaves the maximum unchanged) before reducing, so the pass costs one memory latency.
 __global__ __launch_bounds__(kThreads) void scale_finalize_kernel(const float* __restrict__ partials,
                                                                   int n, float* tscale) {
-  const float a = reduce_partials(partials, n);
+  constexpr int kPer = kMaxPartials / kThreads;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    v[k] = __float_as_uint(partials[min((int)threadIdx.x + k * kThreads, n - 1)]);
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) m = max(m, v[k]);
+  const float a = __uint_as_float(block_max_u32(m));
   if (threadIdx.x == 0) tscale[0] = a / kScaleDenom;
 }
 
@@ -126,8 +140,11 @@ hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bo
   int g;
   if (!hadamard) {
     const int64_t n16 = n / 8;
-    g = grid_for(n16, kUnroll);
-    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n16, partials);
+    int64_t per = (n16 + kMaxPartials - 1) / kMaxPartials;
+    per = per < 1 ? kSlabQuantum : (per + kSlabQuantum - 1) / kSlabQuantum * kSlabQuantum;
+    g = (int)((n16 + per - 1) / per);
+    if (g < 1) g = 1;  // empty tensor: one workgroup writes a zero partial
+    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n16, per, partials);
   } else if (!hadamard_cols) {
     const int64_t nblk = n / 16;
     g = grid_for(nblk, 2);
