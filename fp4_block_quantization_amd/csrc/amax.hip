@@ -3,7 +3,9 @@
 //
 // One streaming pass writes one partial maximum per workgroup into the caller's
 // workspace (plain stores: no atomics, no fences, nothing to clear between calls);
-// a one-workgroup kernel then reduces the partials and writes t.  Each thread folds
+// either a one-workgroup kernel reduces the partials and writes t, or the quantize
+// kernel that follows reduces them in every workgroup (at most 1024 partials: one
+// 16-byte load per thread) and its first workgroup writes t.  Each thread folds
 // |x| into a running maximum (integer max of bf16 bit patterns with the sign cleared:
 // for non-negative floats the bit order is the value order); the wave reduces with
 // lane shuffles and the workgroup through LDS.
@@ -37,27 +39,25 @@ __device__ __forceinline__ void write_partial(uint32_t bits, float* partials) {
   if (threadIdx.x == 0) partials[blockIdx.x] = __uint_as_float(bits);
 }
 
-// No transform: each workgroup reduces one contiguous slab of 16-byte chunks (8
-// bf16), a multiple of 1024 chunks long; every lane issues four independent 16-byte
-// loads per iteration before consuming any.
+// No transform: grid-stride pass over 16-byte chunks (8 bf16); every lane issues
+// four independent 16-byte loads per iteration before consuming any.  At most 512
+// workgroups (two per CU): enough loads in flight to stream at full bandwidth, and
+// few enough partials for every quantize workgroup to reduce them itself.
 constexpr int kUnroll = 4;
-constexpr int64_t kSlabQuantum = (int64_t)kThreads * kUnroll;
+constexpr int kFlatMaxGrid = 512;
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const uint4* __restrict__ x,
-                                                             int64_t n16, int64_t per,
-                                                             float* partials) {
-  const int64_t beg = (int64_t)blockIdx.x * per;
-  const int64_t end = min(beg + per, n16);
+                                                             int64_t n16, float* partials) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   uint32_t m = 0;
-  for (int64_t i = beg + threadIdx.x; i < end; i += kSlabQuantum) {
+  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
     uint4 w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = i + u * kThreads;
-      w[u] = j < end ? x[j] : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < kUnroll; ++u) w[u] = x[i + u * stride];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) m = pk_max_abs4(m, w[u]);
   }
+  for (; i < n16; i += stride) m = pk_max_abs4(m, x[i]);
   const uint32_t bits = max(m & 0xffffu, m >> 16) << 16;
   write_partial(bits, partials);
 }
@@ -68,10 +68,21 @@ __global__ __launch_bounds__(kThreads) void amax_rht_rows_kernel(const uint4* __
                                                                  float* partials) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   float m = 0.0f;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+  int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; b + stride < nblk; b += 2 * stride) {   // two blocks' loads in flight per lane
     const uint4 w0 = x[2 * b], w1 = x[2 * b + 1];
+    const uint4 w2 = x[2 * (b + stride)], w3 = x[2 * (b + stride) + 1];
     float v[16];
     unpack16(w0, w1, v);
+    rht16(v, mask);
+    m = fmaxf(m, amax16(v));
+    unpack16(w2, w3, v);
+    rht16(v, mask);
+    m = fmaxf(m, amax16(v));
+  }
+  if (b < nblk) {
+    float v[16];
+    unpack16(x[2 * b], x[2 * b + 1], v);
     rht16(v, mask);
     m = fmaxf(m, amax16(v));
   }
@@ -107,54 +118,45 @@ __global__ __launch_bounds__(kThreads) void amax_rht_cols_kernel(const uint16_t*
   write_partial(__float_as_uint(m), partials);
 }
 
-// Reduce the partials of the tensor-scale pass and write t.  Every thread issues its
-// loads (n <= 4096 = 16 per thread; indices past n re-read the last partial, which
-// leaves the maximum unchanged) before reducing, so the pass costs one memory latency.
+// Reduce the partials of the tensor-scale pass and write t.
 __global__ __launch_bounds__(kThreads) void scale_finalize_kernel(const float* __restrict__ partials,
                                                                   int n, float* tscale) {
-  constexpr int kPer = kMaxPartials / kThreads;
-  uint32_t v[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k)
-    v[k] = __float_as_uint(partials[min((int)threadIdx.x + k * kThreads, n - 1)]);
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) m = max(m, v[k]);
-  const float a = __uint_as_float(block_max_u32(m));
+  const float a = reduce_partials(partials, n);
   if (threadIdx.x == 0) tscale[0] = a / kScaleDenom;
 }
 
-int grid_for(int64_t work_items, int per_thread) {
+// Workgroups for `work_items` items at `per_thread` items per lane, capped, and
+// rounded up to a multiple of 4 (idle workgroups write a zero partial).
+int grid_for(int64_t work_items, int per_thread, int cap) {
   int64_t g = (work_items + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
   if (g < 1) g = 1;
-  if (g > kMaxPartials) g = kMaxPartials;
-  return (int)g;
+  if (g > cap) g = cap;
+  return (int)((g + 3) & ~3);
 }
 
 }  // namespace
 
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bool hadamard,
                                bool hadamard_cols, uint32_t rht_mask, float* partials,
-                               float* tscale, hipStream_t stream) {
+                               bool finalize, float* tscale, int* npartials,
+                               hipStream_t stream) {
   const int64_t n = rows * cols;
   int g;
   if (!hadamard) {
     const int64_t n16 = n / 8;
-    int64_t per = (n16 + kMaxPartials - 1) / kMaxPartials;
-    per = per < 1 ? kSlabQuantum : (per + kSlabQuantum - 1) / kSlabQuantum * kSlabQuantum;
-    g = (int)((n16 + per - 1) / per);
-    if (g < 1) g = 1;  // empty tensor: one workgroup writes a zero partial
-    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n16, per, partials);
+    g = grid_for(n16, kUnroll, kFlatMaxGrid);
+    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n16, partials);
   } else if (!hadamard_cols) {
     const int64_t nblk = n / 16;
-    g = grid_for(nblk, 2);
+    g = grid_for(nblk, 2, kMaxPartials);
     amax_rht_rows_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, nblk, rht_mask, partials);
   } else {
     const int64_t npatch = (rows / 16) * (cols / 8);
-    g = grid_for(npatch, 1);
+    g = grid_for(npatch, 1, kMaxPartials);
     amax_rht_cols_kernel<<<g, kThreads, 0, stream>>>(x, rows, cols, rht_mask, partials);
   }
-  scale_finalize_kernel<<<1, kThreads, 0, stream>>>(partials, g, tscale);
+  if (finalize) scale_finalize_kernel<<<1, kThreads, 0, stream>>>(partials, g, tscale);
+  if (npartials) *npartials = g;
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ fos_status check_outputs(const fos_quant_config* cfg, int64_t rows, int64_t cols
 fos_status check_scale_and_workspace(const float* tscale, const void* ws, size_t ws_bytes) {
   if (!tscale) return FOS_E_NULL;
   if (!aligned(tscale, 4)) return FOS_E_ALIGN;
-  if (!ws || ws_bytes < kWorkspaceBytes || !aligned(ws, 4)) return FOS_E_WORKSPACE;
+  if (!ws || ws_bytes < kWorkspaceBytes || !aligned(ws, 16)) return FOS_E_WORKSPACE;
   return FOS_OK;
 }
 
@@ -90,6 +90,9 @@ fos::QuantArgs make_args(const fos_quant_config* cfg, const void* x, int64_t row
   a.rows = rows;
   a.cols = cols;
   a.tscale = tscale;
+  a.partials = nullptr;
+  a.npartials = 0;
+  a.tscale_out = nullptr;
   a.row_data = row_data;
   a.row_scales = row_scales;
   a.col_data = col_data;
@@ -106,14 +109,16 @@ fos::QuantArgs make_args(const fos_quant_config* cfg, const void* x, int64_t row
   return a;
 }
 
-// Tensor-scale pass (partial maxima in the workspace, then t into *tscale).
+// Tensor-scale pass: partial maxima into the workspace, their count into *npartials,
+// and (with `finalize`) t into *tscale.
 fos_status launch_scale(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols,
-                        float* tscale, void* ws, hipStream_t s) {
+                        float* tscale, void* ws, bool finalize, int* npartials, hipStream_t s) {
   const bool had = cfg->hadamard != 0;
   const uint32_t mask = had ? hadamard_mask(cfg->hadamard_seed) : 0u;
   const hipError_t e = fos::launch_tensor_scale(static_cast<const uint16_t*>(x), rows, cols, had,
                                                 had && wants_cols(cfg), mask,
-                                                static_cast<float*>(ws), tscale, s);
+                                                static_cast<float*>(ws), finalize, tscale,
+                                                npartials, s);
   return e == hipSuccess ? FOS_OK : FOS_E_HIP;
 }
 
@@ -146,7 +151,7 @@ fos_status fos_tensor_scale(const fos_quant_config* cfg, const void* x, int64_t 
   if ((st = check_input(cfg, x, rows, cols)) != FOS_OK) return st;
   if ((st = check_scale_and_workspace(tensor_scale, workspace, workspace_bytes)) != FOS_OK)
     return st;
-  return launch_scale(cfg, x, rows, cols, tensor_scale, workspace,
+  return launch_scale(cfg, x, rows, cols, tensor_scale, workspace, true, nullptr,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -179,9 +184,18 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
   if ((st = check_outputs(cfg, rows, cols, row_data, row_scales, col_data, col_scales)) != FOS_OK)
     return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = launch_scale(cfg, x, rows, cols, tensor_scale, workspace, s)) != FOS_OK) return st;
-  const fos::QuantArgs a =
-      make_args(cfg, x, rows, cols, tensor_scale, row_data, row_scales, col_data, col_scales);
+  // an empty tensor launches no quantize kernel: the scale pass writes t (= 0) itself
+  const bool empty = rows * cols == 0;
+  int npartials = 0;
+  if ((st = launch_scale(cfg, x, rows, cols, tensor_scale, workspace, empty, &npartials, s)) !=
+      FOS_OK)
+    return st;
+  if (empty) return FOS_OK;
+  fos::QuantArgs a =
+      make_args(cfg, x, rows, cols, nullptr, row_data, row_scales, col_data, col_scales);
+  a.partials = static_cast<const float*>(workspace);
+  a.npartials = npartials;
+  a.tscale_out = tensor_scale;
   return fos::launch_quantize(a, s) == hipSuccess ? FOS_OK : FOS_E_HIP;
 }
 

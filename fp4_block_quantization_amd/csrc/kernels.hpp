@@ -9,7 +9,10 @@ namespace fos {
 struct QuantArgs {
   const uint16_t* x;        // bf16 [rows][cols]
   int64_t rows, cols;
-  const float* tscale;      // device fp32 t
+  const float* tscale;      // device fp32 t (read when `partials` is null)
+  const float* partials;    // tensor-scale partial maxima: when set, every workgroup
+  int npartials;            //   reduces them to t itself and workgroup 0 writes t to
+  float* tscale_out;        //   *tscale_out (fused finish of the tensor-scale pass)
   uint8_t* row_data;        // [rows][cols/2]   (may be null when not requested)
   uint8_t* row_scales;      // [rows][cols/16]
   uint8_t* col_data;        // [cols][rows/2]
@@ -23,11 +26,14 @@ struct QuantArgs {
   bool hadamard;
 };
 
-// Tensor-scale pass: one partial max|x| per workgroup into `partials` (at most
-// kMaxPartials), then a one-workgroup kernel writes t = max / 2688 to *tscale.
+// Tensor-scale pass: one partial max|x| per workgroup into `partials` (16-byte
+// aligned; the count, a multiple of 4 and at most kMaxPartials, goes to *npartials).
+// With `finalize`, a one-workgroup kernel then writes t = max / 2688 to *tscale;
+// without it the quantize kernel finishes the reduction (QuantArgs::partials).
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bool hadamard,
                                bool hadamard_cols, uint32_t rht_mask, float* partials,
-                               float* tscale, hipStream_t stream);
+                               bool finalize, float* tscale, int* npartials,
+                               hipStream_t stream);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 

@@ -28,10 +28,18 @@ struct TensorConsts {
   float t, u6, u4;
 };
 
-// t from the caller's device scalar (written by the tensor-scale pass).
+// t from the caller's device scalar, or (fused finish of the tensor-scale pass)
+// from the pass's partial maxima, reduced by every workgroup; workgroup 0 stores t.
+// Every thread of the workgroup must call this (it synchronizes the workgroup);
+// callers issue their input loads first so that the reduction overlaps them.
 __device__ __forceinline__ TensorConsts tensor_consts(const QuantArgs& a) {
   TensorConsts c;
-  c.t = a.tscale[0];
+  if (a.partials) {
+    c.t = reduce_partials(a.partials, a.npartials) / kScaleDenom;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.tscale_out[0] = c.t;
+  } else {
+    c.t = a.tscale[0];
+  }
   c.u6 = 1.0f / (c.t * 6.0f);
   c.u4 = 1.0f / (c.t * 4.0f);
   return c;
@@ -50,7 +58,6 @@ constexpr int kRowsPerWG = 2 * kThreads;
 
 template <bool k46, bool kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
-  const TensorConsts tc = tensor_consts(a);
   const uint4* __restrict__ x = reinterpret_cast<const uint4*>(a.x);
   const int64_t b0 = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
   uint4 w[4];
@@ -64,6 +71,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
       w[2 * q + 1] = x[2 * b + 1];
     }
   }
+  const TensorConsts tc = tensor_consts(a);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int64_t b = b0 + q * kThreads;
@@ -91,20 +99,29 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
   const int64_t R0 = (int64_t)(blockIdx.x / tiles_c) * kTileR;
   const int64_t C0 = (int64_t)(blockIdx.x % tiles_c) * kTileC;
   const int tid = threadIdx.x;
-  const TensorConsts tc = tensor_consts(a);
 
+  // all eight 16-byte loads of the lane are in flight before anything waits on them
   const int j = tid & 3;
+  uint4 w[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = (tid >> 2) + 64 * k;
+    const int64_t gr = R0 + row, gc = C0 + 16 * j;
+    w[2 * k] = make_uint4(0, 0, 0, 0);
+    w[2 * k + 1] = w[2 * k];
+    if (gr < R && gc < C) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
+      w[2 * k] = p[0];
+      w[2 * k + 1] = p[1];
+    }
+  }
+  const TensorConsts tc = tensor_consts(a);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int row = (tid >> 2) + 64 * k;
     const int64_t gr = R0 + row, gc = C0 + 16 * j;
     const bool ok = gr < R && gc < C;
-    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-    if (ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
-      w0 = p[0];
-      w1 = p[1];
-    }
+    const uint4 w0 = w[2 * k], w1 = w[2 * k + 1];
     const int sw = 4 * ((row >> 4) & 7);
     *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j) ^ sw)]) = w0;
     *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j + 4) ^ sw)]) = w1;
@@ -161,16 +178,16 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   const int row = tid & 15, tl = tid >> 4;
   const int64_t T = (int64_t)(blockIdx.x % wg_per_row) * 16 + tl;
   const bool valid = T < tiles_c;
-  const TensorConsts tc = tensor_consts(a);
 
-  float v[16];
+  uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
   if (valid) {
     const uint4* p = reinterpret_cast<const uint4*>(a.x + (R0 + row) * C + 16 * T);
-    unpack16(p[0], p[1], v);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    w0 = p[0];
+    w1 = p[1];
   }
+  const TensorConsts tc = tensor_consts(a);
+  float v[16];
+  unpack16(w0, w1, v);
   float kk[16];
   const int64_t rblk = (R0 + row) * tiles_c + T;    // row-wise block id of this row
   if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, kk);

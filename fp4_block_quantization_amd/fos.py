@@ -108,8 +108,8 @@ _workspaces = {}
 
 
 def workspace(device: torch.device) -> torch.Tensor:
-    """Zero-filled workspace for the current stream of ``device`` (one per stream;
-    the library leaves it zero-filled after every call)."""
+    """Scratch workspace for the current stream of ``device`` (one per stream, so
+    that calls on different streams never share one; its contents are scratch)."""
     device = torch.device(device)
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)

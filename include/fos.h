@@ -54,7 +54,8 @@ typedef enum {
                           aligned, or an output buffer misaligned                   */
   FOS_E_FLAGS = 4,     /* unknown enum value, wrong struct_size, or an unsupported
                           option combination (e.g. Hadamard with 2D blocks)         */
-  FOS_E_WORKSPACE = 5, /* workspace NULL or smaller than fos_workspace_bytes()      */
+  FOS_E_WORKSPACE = 5, /* workspace NULL, not 16-byte aligned, or smaller than
+                          fos_workspace_bytes()                                     */
   FOS_E_HIP = 6        /* a HIP launch failed                                        */
 } fos_status;
 
@@ -96,8 +97,9 @@ int fos_abi_version(void);
 const char* fos_status_string(fos_status status);
 
 /* Bytes of device workspace that fos_tensor_scale / fos_quantize need (scratch for
- * the per-workgroup partial maxima of the tensor-scale pass; its contents on entry
- * are ignored, and it must stay untouched until the call's kernels have run). */
+ * the per-workgroup partial maxima of the tensor-scale pass, 16-byte aligned; its
+ * contents on entry are ignored, and it must stay untouched until the call's
+ * kernels have run). */
 size_t fos_workspace_bytes(void);
 
 /* Per-tensor scale.  Writes t = RN_fp32(A / 2688) to *tensor_scale (device fp32),
@@ -128,8 +130,9 @@ fos_status fos_quantize_scaled(const fos_quant_config* cfg, const void* x, int64
                                uint8_t* row_data, uint8_t* row_scales,
                                uint8_t* col_data, uint8_t* col_scales, void* stream);
 
-/* fos_tensor_scale followed by fos_quantize_scaled on the same stream; the tensor
- * scale is written to *tensor_scale. */
+/* fos_tensor_scale followed by fos_quantize_scaled on the same stream, with the same
+ * results; the tensor scale is written to *tensor_scale.  (The partial maxima of the
+ * scale pass are reduced inside the quantize kernel, which saves one launch.) */
 fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows,
                         int64_t cols, uint8_t* row_data, uint8_t* row_scales,
                         uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,

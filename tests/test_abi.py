@@ -67,6 +67,7 @@ def q(c, x=FAKE, rows=64, cols=64, rd=FAKE, rs=FAKE, cd=FAKE, cs=FAKE, t=FAKE, w
     ({}, dict(t=None), fos.FOS_E_NULL),
     ({}, dict(ws=None), fos.FOS_E_WORKSPACE),
     ({}, dict(wsb=4), fos.FOS_E_WORKSPACE),
+    ({}, dict(ws=ctypes.c_void_p(0x100008)), fos.FOS_E_WORKSPACE),   # not 16-byte aligned
     (dict(raw={"rule": 7}), {}, fos.FOS_E_FLAGS),
     (dict(raw={"rounding": 2}), {}, fos.FOS_E_FLAGS),
     (dict(raw={"outputs": 0}), {}, fos.FOS_E_FLAGS),

@@ -191,6 +191,30 @@ def test_quantize_scaled_with_given_scale(fos):
     assert_quant_equal(gpu_quantize(fos, bits, cfg, tensor_scale=t), o)
 
 
+@pytest.mark.parametrize("cfg_name", ["row", "row_rht", "col_rht", "rowcol", "2d"])
+@pytest.mark.parametrize("shape", [(16, 16), (272, 1040), (4096, 4112)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_fused_scale_matches_two_step(fos, cfg_name, shape):
+    """fos_quantize reduces the scale pass's partial maxima inside the quantize kernel;
+    it must give what fos_tensor_scale + fos_quantize_scaled give, and the oracle's t.
+    The shapes span one to the maximum number of partials."""
+    cfg = CFGS[cfg_name]
+    bits = bits_of(W.random_bf16(*shape, seed=31, dist="student_t"))
+    x = to_gpu_bf16(bits)
+    outs = [o for o, on in (("row", cfg.rows_out), ("col", cfg.cols_out)) if on]
+    seed = cfg.hadamard_seed if cfg.hadamard else None
+    t2 = fos.tensor_scale(x, hadamard_seed=seed, outputs=outs)
+    torch.cuda.synchronize()
+    fused = gpu_quantize(fos, bits, cfg)
+    two = gpu_quantize(fos, bits, cfg, tensor_scale=t2)
+    t_oracle = N.prepare(bits, cfg)[1]
+    assert fused["t"].view(np.uint32) == np.float32(t_oracle).view(np.uint32)
+    assert fused["t"].view(np.uint32) == np.float32(t2.cpu().numpy()[0]).view(np.uint32)
+    for k in fused:
+        if k != "t":
+            assert_same_bytes(fused[k], two[k], k)
+
+
 def test_deterministic(fos):
     bits = bits_of(W.random_bf16(512, 1024, 9, "student_t"))
     for cfg in (CFGS["rowcol_sr"], CFGS["2d"], CFGS["row_rht_sr"]):
