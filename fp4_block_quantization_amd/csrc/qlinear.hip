@@ -14,15 +14,16 @@
 //
 // Tiling: a 256-thread workgroup owns a 256x256 tile of Y, each wave a 128x128
 // quarter held as 4x4 MFMA accumulators (256 fp32 per lane).  Both operands are
-// K-major, so a lane's 8 MFMA k-slots come from one 4-byte word of packed nibbles:
-// for a 64-wide K chunk, lane half h (lane / 32) takes the 32 consecutive k values
-// [32h, 32h + 32) in one 16-byte load per row, and k-step j uses word j.  A and B use
-// the same k mapping, so the reordering of k inside the chunk cancels in the sum.
-// No LDS is used: each wave reads its packed operands straight from L2 (the 2x
-// re-read within a workgroup is 4 KB per wave per chunk); three register stages keep
-// the next two chunks in flight while the current one is multiplied.  Workgroups are
-// remapped so that each XCD (dispatched round-robin) runs a contiguous group of
-// 4 tile-rows x all tile-columns.
+// K-major, so a lane's 8 MFMA k-slots come from one 4-byte word of packed nibbles; A
+// and B use the same k mapping, so the reordering of k inside a chunk cancels in the
+// sum.  Two kernels:
+//   qlinear_lds_kernel (K % 256 == 0): packed operands are copied global -> LDS in
+//     256-wide K stages (double-buffered) and dequantized from LDS, software-pipelined
+//     against the MFMAs;
+//   qlinear_kernel (any K % 64 == 0): each wave reads its packed operands straight
+//     from L2 into registers, three register stages deep.
+// Workgroups are remapped so that each XCD (dispatched round-robin) runs a contiguous
+// group of 4 tile-rows x all tile-columns.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -49,8 +50,11 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// ---------------------------------------------------------------- register-staged kernel
 // Packed operands of one 64-wide K chunk for one lane: 16 bytes of nibbles per A row
-// tile and per B column tile, and the two E4M3 scale bytes that cover them.
+// tile and per B column tile, and the two E4M3 scale bytes that cover them.  Lane
+// half h (lane / 32) takes the 32 consecutive k values [32h, 32h + 32) of the chunk
+// in one 16-byte load per row, and k-step j uses word j of it.
 template <int TI, int TJ>
 struct Stage {
   uint4 a[TI], b[TJ];
@@ -296,9 +300,8 @@ __device__ __forceinline__ uint4 lds_granule(const uint8_t* base, int row, int g
   return *reinterpret_cast<const uint4*>(base + row * kRowBytes + ((g ^ ((row >> 1) & 7)) << 4));
 }
 
-// Multiply one super-chunk held in LDS: 4 granule groups x 4 MFMA k-steps.  The
-// next group's granules are read from LDS before the current group's last 16 MFMAs;
-// scheduling barriers between groups keep the register footprint to one group.
+// E4M3 scale pairs of granule group gq as fp16 pairs (d[i][0] for the group's first 16
+// k values, d[i][1] for the next 16).
 __device__ __forceinline__ void group_scales(const uint2 (&sc)[4], int gq, h2 (&d)[4][2]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -309,10 +312,15 @@ __device__ __forceinline__ void group_scales(const uint2 (&sc)[4], int gq, h2 (&
   }
 }
 
-__device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4], int ra, int rb,
-                                          int h) {
+// Multiply one super-chunk held in LDS: 16 k-steps of 16 MFMAs (4 granule groups of
+// 4 k-steps).  Software-pipelined: the operands of k-step s + 1 are dequantized while
+// the 16 MFMAs of k-step s issue (one MFMA, then up to five VALU instructions,
+// repeated), so the conversion runs in the MFMA pipe's shadow instead of in front of
+// it; the next group's granules are read from LDS three k-steps before they are used.
+__device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4], int ra,
+                                               int rb, int h) {
   uint2 sca[4], scb[4];
-  uint4 ga[4], gb[4];
+  uint4 ga[4], gb[4], na[4], nb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sca[i] = *reinterpret_cast<const uint2*>(st.sa + (ra + 32 * i) * kRowScales + 8 * h);
@@ -320,39 +328,61 @@ __device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4
     ga[i] = lds_granule(st.a, ra + 32 * i, 4 * h);
     gb[i] = lds_granule(st.b, rb + 32 * i, 4 * h);
   }
+  h2 da[4][2], db[4][2];
+  group_scales(sca, 0, da);
+  group_scales(scb, 0, db);
+  h8 A[4], B[4];
 #pragma unroll
-  for (int gq = 0; gq < 4; ++gq) {
-    h2 da[4][2], db[4][2];
-    group_scales(sca, gq, da);
-    group_scales(scb, gq, db);
-    uint4 na[4], nb[4];
+  for (int i = 0; i < 4; ++i) {
+    A[i] = dequant8(word(ga[i], 0), da[i][0]);
+    B[i] = dequant8(word(gb[i], 0), db[i][0]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      h8 A[4], B[4];
+  for (int s = 0; s < 16; ++s) {
+    const int gq = s >> 2, jj = s & 3;
+    if (jj == 0 && gq < 3) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        A[i] = dequant8(word(ga[i], jj), da[i][jj >> 1]);
-        B[i] = dequant8(word(gb[i], jj), db[i][jj >> 1]);
+        na[i] = lds_granule(st.a, ra + 32 * i, 4 * h + gq + 1);
+        nb[i] = lds_granule(st.b, rb + 32 * i, 4 * h + gq + 1);
       }
-      if (jj == 3 && gq < 3) {
+    }
+    h8 An[4], Bn[4];
+    if (s < 15) {
+      const int gq1 = (s + 1) >> 2, jj1 = (s + 1) & 3;
+      if (jj1 == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          na[i] = lds_granule(st.a, ra + 32 * i, 4 * h + gq + 1);
-          nb[i] = lds_granule(st.b, rb + 32 * i, 4 * h + gq + 1);
+          ga[i] = na[i];
+          gb[i] = nb[i];
         }
+        group_scales(sca, gq1, da);
+        group_scales(scb, gq1, db);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[n], acc[i][n], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; ++i) {
+        An[i] = dequant8(word(ga[i], jj1), da[i][jj1 >> 1]);
+        Bn[i] = dequant8(word(gb[i], jj1), db[i][jj1 >> 1]);
+      }
     }
-    if (gq < 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[n], acc[i][n], 0, 0, 0);
+    if (jj == 0 && gq < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s < 15) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ga[i] = na[i];
-        gb[i] = nb[i];
+        A[i] = An[i];
+        B[i] = Bn[i];
       }
     }
   }
