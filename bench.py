@@ -239,7 +239,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
-                    help="profiling aid: run one piece (c2_step, c2_kernel, copy) and exit")
+                    help="profiling aid: run one piece (c2_step, c2_kernel, c5_qlinear, copy) and exit")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -255,6 +255,15 @@ def main():
     x2 = W.make("c2")
 
     if args.only is not None:
+        if args.only == "c5_qlinear":
+            xq = fos.quantize(W.make("c5_x").to("cuda:0"))
+            wq = fos.quantize(W.make("c5_w").to("cuda:0"))
+            y = fos.qlinear_fwd(xq, wq)
+            for _ in range(args.steps):
+                fos.qlinear_fwd(xq, wq, out=y)
+            torch.cuda.synchronize()
+            log(f"ran c5_qlinear x{args.steps}")
+            return
         if args.only == "copy":
             a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
             b = torch.empty_like(a)

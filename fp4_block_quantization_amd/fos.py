@@ -232,13 +232,20 @@ def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.float32) -> torch.Tens
     return out
 
 
-def qlinear_fwd(xq: NVFP4Tensor, wq: NVFP4Tensor) -> torch.Tensor:
-    """Y = deq(Xq) deq(Wq)^T in bf16; Xq [M, K] and Wq [N, K] row-wise records."""
+def qlinear_fwd(xq: NVFP4Tensor, wq: NVFP4Tensor, out: Optional[torch.Tensor] = None
+                ) -> torch.Tensor:
+    """Y = deq(A) deq(B)^T in bf16 for two records blocked along their shared inner
+    dimension: A [M, K], B [N, K] as stored (a column-wise record of W is the record
+    of W^T; 2D records carry one scale per 16 values too).  ``out``: optional bf16
+    [M, N] destination."""
     M, K = xq.shape
     N, K2 = wq.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
-    y = torch.empty(M, N, dtype=torch.bfloat16, device=xq.data.device)
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16,
+                                                device=xq.data.device)
+    if y.shape != (M, N) or y.dtype != torch.bfloat16 or not y.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
     fos_qlinear_fwd(xq.data, xq.scales, xq.tensor_scale, wq.data, wq.scales, wq.tensor_scale,
                     M, N, K, y)
     return y
