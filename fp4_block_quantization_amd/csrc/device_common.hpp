@@ -12,6 +12,7 @@
 //   r   = a * u_c                 (a = block max |x|; r = 0 when a == 0)
 //   S   = E4M3 RNE saturating(r), D = value(S), d = D * t
 //   inv = 1 / d, or 0 when d is zero or subnormal (every value becomes a signed 0)
+//         (d and inv are per tensor and code: looked up in a per-workgroup table)
 //   v_i = x_i * inv, code = E2M1 RNE(v_i) (hardware cvt, saturating at 6) or the
 //         stochastic rounding below
 //   e_i = fma(E(code_i), d, -x_i) (the exact error rounded once)
@@ -177,13 +178,32 @@ struct Cand {
   float d;        // block decode scale D * t
 };
 
+// Per-tensor table of the decode scale and element reciprocal of every E4M3 code:
+// entry S holds (d, inv) with d = D(S) * t and inv = 1 / d, or 0 when d is zero or
+// subnormal; entry 128 holds (u6, u4) = (1 / (t * 6), 1 / (t * 4)).  d takes one of
+// at most 127 values per tensor, so each workgroup computes the divisions once here
+// instead of twice per block.  Built by a workgroup of at least 129 threads; ends
+// with a workgroup barrier.
+constexpr int kScaleTableSize = 129;
+__device__ __forceinline__ void build_scale_table(float2* tab, float t) {
+  const int i = threadIdx.x;
+  if (i < 128) {
+    const float d = e4m3_decode((uint32_t)i) * t;
+    tab[i] = make_float2(d, (d >= kMinNormal) ? 1.0f / d : 0.0f);
+  } else if (i == 128) {
+    tab[128] = make_float2(1.0f / (t * 6.0f), 1.0f / (t * 4.0f));
+  }
+  __syncthreads();
+}
+
 // Scale byte, decode scale and element reciprocal of a candidate (per block).
-__device__ __forceinline__ void cand_scale(float a, float t, float u, uint32_t& s, float& d,
-                                           float& inv) {
+__device__ __forceinline__ void cand_scale(float a, float u, const float2* tab, uint32_t& s,
+                                           float& d, float& inv) {
   const float r = (a == 0.0f) ? 0.0f : a * u;
   s = e4m3_encode(r);
-  d = e4m3_decode(s) * t;
-  inv = (d >= kMinNormal) ? 1.0f / d : 0.0f;
+  const float2 e = tab[s];
+  d = e.x;
+  inv = e.y;
 }
 
 // Round-to-nearest-even codes of 16 values with the hardware conversion, and the
@@ -247,15 +267,15 @@ __device__ __forceinline__ float amax16(const float (&x)[16]) {
 
 // Quantize one 1D block with both candidates (or 6 alone) and return the winner.
 template <bool kFourOverSix, bool kSR>
-__device__ __forceinline__ Cand quantize_block(const float (&x)[16], float t, float u6,
-                                               float u4, const float (&kk)[16]) {
+__device__ __forceinline__ Cand quantize_block(const float (&x)[16], const float2* tab,
+                                               float u6, float u4, const float (&kk)[16]) {
   const float a = amax16(x);
   Cand c6, c4;
   float inv6, inv4;
-  cand_scale(a, t, u6, c6.s, c6.d, inv6);
+  cand_scale(a, u6, tab, c6.s, c6.d, inv6);
   if (kSR) cand_codes_sr(x, c6.d, inv6, kk, c6); else cand_codes_rne(x, c6.d, inv6, c6);
   if (!kFourOverSix) return c6;
-  cand_scale(a, t, u4, c4.s, c4.d, inv4);
+  cand_scale(a, u4, tab, c4.s, c4.d, inv4);
   if (kSR) cand_codes_sr(x, c4.d, inv4, kk, c4); else cand_codes_rne(x, c4.d, inv4, c4);
   return (c4.err < c6.err) ? c4 : c6;
 }

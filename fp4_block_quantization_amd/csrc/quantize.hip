@@ -25,23 +25,29 @@ namespace {
 constexpr int kThreads = 256;
 
 struct TensorConsts {
-  float t, u6, u4;
+  const float2* tab;   // per-code (d, inv), in LDS
+  float u6, u4;
 };
 
 // t from the caller's device scalar, or (fused finish of the tensor-scale pass)
 // from the pass's partial maxima, reduced by every workgroup; workgroup 0 stores t.
-// Every thread of the workgroup must call this (it synchronizes the workgroup);
-// callers issue their input loads first so that the reduction overlaps them.
-__device__ __forceinline__ TensorConsts tensor_consts(const QuantArgs& a) {
-  TensorConsts c;
+// Then the workgroup's scale table.  Every thread of the workgroup must call this
+// (it synchronizes the workgroup); callers issue their input loads first so that
+// this overlaps them.
+__device__ __forceinline__ TensorConsts tensor_consts(const QuantArgs& a, float2* tab) {
+  float t;
   if (a.partials) {
-    c.t = reduce_partials(a.partials, a.npartials) / kScaleDenom;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.tscale_out[0] = c.t;
+    t = reduce_partials(a.partials, a.npartials) / kScaleDenom;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.tscale_out[0] = t;
   } else {
-    c.t = a.tscale[0];
+    t = a.tscale[0];
   }
-  c.u6 = 1.0f / (c.t * 6.0f);
-  c.u4 = 1.0f / (c.t * 4.0f);
+  build_scale_table(tab, t);
+  TensorConsts c;
+  c.tab = tab;
+  const float2 u = tab[128];
+  c.u6 = u.x;
+  c.u4 = u.y;
   return c;
 }
 
@@ -71,7 +77,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
       w[2 * q + 1] = x[2 * b + 1];
     }
   }
-  const TensorConsts tc = tensor_consts(a);
+  __shared__ float2 tab[kScaleTableSize];
+  const TensorConsts tc = tensor_consts(a, tab);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int64_t b = b0 + q * kThreads;
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
     if (kRHT) rht16(v, a.rht_mask);
     float kk[16];
     if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, kk);
-    const Cand c = quantize_block<k46, kSR>(v, tc.t, tc.u6, tc.u4, kk);
+    const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, kk);
     store_block(a.row_data, a.row_scales, 8 * b, b, c);
   }
 }
@@ -115,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
       w[2 * k + 1] = p[1];
     }
   }
-  const TensorConsts tc = tensor_consts(a);
+  __shared__ float2 tab[kScaleTableSize];
+  const TensorConsts tc = tensor_consts(a, tab);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int row = (tid >> 2) + 64 * k;
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
       float kk[16];
       const int64_t blk = gr * (C / 16) + gc / 16;
       if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, kk);
-      const Cand c = quantize_block<k46, kSR>(v, tc.t, tc.u6, tc.u4, kk);
+      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, kk);
       store_block(a.row_data, a.row_scales, 8 * blk, blk, c);
     }
   }
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
       const int64_t blk = col * nrb + gr0 / 16;
       float kk[16];
       if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, kk);
-      const Cand c = quantize_block<k46, kSR>(v, tc.t, tc.u6, tc.u4, kk);
+      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, kk);
       store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
     }
   }
@@ -185,7 +193,8 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
     w0 = p[0];
     w1 = p[1];
   }
-  const TensorConsts tc = tensor_consts(a);
+  __shared__ float2 tab[kScaleTableSize];
+  const TensorConsts tc = tensor_consts(a, tab);
   float v[16];
   unpack16(w0, w1, v);
   float kk[16];
@@ -198,13 +207,13 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
 
   Cand c6, c4;
   float inv6, inv4;
-  cand_scale(am, tc.t, tc.u6, c6.s, c6.d, inv6);
+  cand_scale(am, tc.u6, tc.tab, c6.s, c6.d, inv6);
   if (kSR) cand_codes_sr(v, c6.d, inv6, kk, c6); else cand_codes_rne(v, c6.d, inv6, c6);
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) c6.err = c6.err + __shfl_xor(c6.err, m);
   Cand c = c6;
   if (k46) {
-    cand_scale(am, tc.t, tc.u4, c4.s, c4.d, inv4);
+    cand_scale(am, tc.u4, tc.tab, c4.s, c4.d, inv4);
     if (kSR) cand_codes_sr(v, c4.d, inv4, kk, c4); else cand_codes_rne(v, c4.d, inv4, c4);
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) c4.err = c4.err + __shfl_xor(c4.err, m);
