@@ -121,36 +121,33 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-// Stochastic-rounding draws of one block: byte i of the 16 Philox output bytes,
-// returned as k_i + 0.5 (exact in fp32).  Counter = (b_lo, b_hi, 0, stream).
+// Stochastic-rounding draws of one block: byte k_i of the 16 Philox output bytes,
+// returned as the threshold q_i = (k_i + 0.5) / 256 (exact in fp32).  Counter =
+// (b_lo, b_hi, 0, stream).
 __device__ __forceinline__ void sr_draws(uint64_t block, uint32_t stream, uint32_t k0,
-                                         uint32_t k1, float (&kk)[16]) {
+                                         uint32_t k1, float (&q)[16]) {
   const uint4 w = philox4x32_10(make_uint4((uint32_t)block, (uint32_t)(block >> 32), 0u, stream),
                                 k0, k1);
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    kk[i] = (float)((words[i >> 2] >> (8 * (i & 3))) & 0xffu) + 0.5f;
+    q[i] = __builtin_fmaf((float)((words[i >> 2] >> (8 * (i & 3))) & 0xffu), 0x1p-8f, 0x1p-9f);
 }
 
-// Stochastic rounding of f = |v| >= 0 onto the E2M1 grid.  Scaling by s in
-// {2, 1, 1/2} makes the grid spacing 1 inside f's interval ([0,2), [2,4), [4,6]);
-// p = fractional position (exact); round up iff (k + 0.5)/256 < p.  Returns the
-// magnitude code; g receives the grid value.
-__device__ __forceinline__ uint32_t e2m1_sr(float f, float kk, float& g) {
+// Stochastic rounding of f = |v| >= 0 onto the E2M1 magnitudes; returns the grid
+// value.  With e = max(exponent of f, 1) (f = m 2^e, m in [0.5, 1)), y = f 2^(2-e)
+// maps f's grid interval ([0,2), [2,4) or [4,6]) onto unit spacing, so y = yl + p
+// with p the exact fractional position.  Rounding up iff q < p (q = (k + 0.5)/256)
+// is ceil(y - q): it gives yl + 1 when p > q and yl when p <= q.  y - q is exact
+// whenever it lies near an integer (y >= 1 has no bits below 2^-22 and q is a
+// multiple of 2^-9; for y < 1 the result stays strictly inside (-1, 1)), so its
+// fp32 rounding never moves the ceiling.  Saturates at 6.
+__device__ __forceinline__ float e2m1_sr_mag(float f, float q) {
   f = fminf(f, 6.0f);
-  const bool b0 = f < 2.0f, b1 = f < 4.0f;
-  const float s = b0 ? 2.0f : (b1 ? 1.0f : 0.5f);
-  const float si = b0 ? 0.5f : (b1 ? 1.0f : 2.0f);
-  const uint32_t off = b0 ? 0u : (b1 ? 2u : 4u);
-  const float y = f * s;
-  const float yl = floorf(y);
-  const float p = y - yl;
-  const float yq = (kk < p * 256.0f) ? yl + 1.0f : yl;
-  g = yq * si;
-  return (uint32_t)yq + off;
+  const int e = max(__builtin_amdgcn_frexp_expf(f), 1);
+  const float y = __builtin_ldexpf(f, 2 - e);
+  return __builtin_ldexpf(__builtin_ceilf(y - q), e - 2);
 }
-
 // ---- random-sign 16-point Hadamard transform ---------------------------------------
 // y_k = x_k * (+-1/4) (sign k from bit k of `mask`), then butterflies with strides
 // 1, 2, 4, 8: (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h).
@@ -237,19 +234,28 @@ __device__ __forceinline__ void cand_codes_rne(const float (&x)[16], float d, fl
   c.err = err;
 }
 
-// Stochastic-rounding codes (software) and the sequential squared error.
+// Stochastic-rounding codes and the sequential squared error.  Each value is first
+// rounded to an exact grid value (with x's sign, so that values rounding to zero
+// keep it); the hardware RNE conversion of an exact grid value is that value's code.
 __device__ __forceinline__ void cand_codes_sr(const float (&x)[16], float d, float inv,
-                                              const float (&kk)[16], Cand& c) {
+                                              const float (&q)[16], Cand& c) {
+  float g[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    g[i] = __builtin_copysignf(e2m1_sr_mag(fabsf(x[i] * inv), q[i]), x[i]);
   uint32_t lo = 0, hi = 0;
+  lo = cvt_pk_fp4<0>(lo, g[0], g[1]);
+  lo = cvt_pk_fp4<1>(lo, g[2], g[3]);
+  lo = cvt_pk_fp4<2>(lo, g[4], g[5]);
+  lo = cvt_pk_fp4<3>(lo, g[6], g[7]);
+  hi = cvt_pk_fp4<0>(hi, g[8], g[9]);
+  hi = cvt_pk_fp4<1>(hi, g[10], g[11]);
+  hi = cvt_pk_fp4<2>(hi, g[12], g[13]);
+  hi = cvt_pk_fp4<3>(hi, g[14], g[15]);
   float err = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float v = x[i] * inv;
-    float g;
-    const uint32_t m = e2m1_sr(fabsf(v), kk[i], g);
-    const uint32_t q = m | ((__float_as_uint(x[i]) >> 28) & 8u);
-    if (i < 8) lo |= q << (4 * i); else hi |= q << (4 * (i - 8));
-    const float e = __builtin_fmaf(g, d, -fabsf(x[i]));
+    const float e = __builtin_fmaf(g[i], d, -x[i]);
     err = __builtin_fmaf(e, e, err);
   }
   c.lo = lo;
@@ -268,15 +274,15 @@ __device__ __forceinline__ float amax16(const float (&x)[16]) {
 // Quantize one 1D block with both candidates (or 6 alone) and return the winner.
 template <bool kFourOverSix, bool kSR>
 __device__ __forceinline__ Cand quantize_block(const float (&x)[16], const float2* tab,
-                                               float u6, float u4, const float (&kk)[16]) {
+                                               float u6, float u4, const float (&srq)[16]) {
   const float a = amax16(x);
   Cand c6, c4;
   float inv6, inv4;
   cand_scale(a, u6, tab, c6.s, c6.d, inv6);
-  if (kSR) cand_codes_sr(x, c6.d, inv6, kk, c6); else cand_codes_rne(x, c6.d, inv6, c6);
+  if (kSR) cand_codes_sr(x, c6.d, inv6, srq, c6); else cand_codes_rne(x, c6.d, inv6, c6);
   if (!kFourOverSix) return c6;
   cand_scale(a, u4, tab, c4.s, c4.d, inv4);
-  if (kSR) cand_codes_sr(x, c4.d, inv4, kk, c4); else cand_codes_rne(x, c4.d, inv4, c4);
+  if (kSR) cand_codes_sr(x, c4.d, inv4, srq, c4); else cand_codes_rne(x, c4.d, inv4, c4);
   return (c4.err < c6.err) ? c4 : c6;
 }
 

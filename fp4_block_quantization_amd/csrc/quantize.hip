@@ -86,9 +86,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
     float v[16];
     unpack16(w[2 * q], w[2 * q + 1], v);
     if (kRHT) rht16(v, a.rht_mask);
-    float kk[16];
-    if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, kk);
-    const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, kk);
+    float srq[16];
+    if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srq);
+    const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
     store_block(a.row_data, a.row_scales, 8 * b, b, c);
   }
 }
@@ -136,10 +136,10 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
     if (kRows && ok) {
       float v[16];
       unpack16(w0, w1, v);
-      float kk[16];
+      float srq[16];
       const int64_t blk = gr * (C / 16) + gc / 16;
-      if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, kk);
-      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, kk);
+      if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srq);
+      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
       store_block(a.row_data, a.row_scales, 8 * blk, blk, c);
     }
   }
@@ -166,9 +166,9 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
       const int64_t col = gc + s;
       if (kRHT) rht16(v, a.rht_mask);
       const int64_t blk = col * nrb + gr0 / 16;
-      float kk[16];
-      if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, kk);
-      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, kk);
+      float srq[16];
+      if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srq);
+      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
       store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
     }
   }
@@ -197,9 +197,9 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   const TensorConsts tc = tensor_consts(a, tab);
   float v[16];
   unpack16(w0, w1, v);
-  float kk[16];
+  float srq[16];
   const int64_t rblk = (R0 + row) * tiles_c + T;    // row-wise block id of this row
-  if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, kk);
+  if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srq);
 
   float am = amax16(v);
 #pragma unroll
@@ -208,13 +208,13 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   Cand c6, c4;
   float inv6, inv4;
   cand_scale(am, tc.u6, tc.tab, c6.s, c6.d, inv6);
-  if (kSR) cand_codes_sr(v, c6.d, inv6, kk, c6); else cand_codes_rne(v, c6.d, inv6, c6);
+  if (kSR) cand_codes_sr(v, c6.d, inv6, srq, c6); else cand_codes_rne(v, c6.d, inv6, c6);
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) c6.err = c6.err + __shfl_xor(c6.err, m);
   Cand c = c6;
   if (k46) {
     cand_scale(am, tc.u4, tc.tab, c4.s, c4.d, inv4);
-    if (kSR) cand_codes_sr(v, c4.d, inv4, kk, c4); else cand_codes_rne(v, c4.d, inv4, c4);
+    if (kSR) cand_codes_sr(v, c4.d, inv4, srq, c4); else cand_codes_rne(v, c4.d, inv4, c4);
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) c4.err = c4.err + __shfl_xor(c4.err, m);
     if (c4.err < c6.err) c = c4;
