@@ -94,24 +94,33 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
 }
 
 // ------------------------------------------------------------------ column-wise tiles
-constexpr int kTileR = 256, kTileC = 64;
+// A TR x 64 tile (TR = 128 or 256 rows) is read once: each lane loads TR/64 rows x 16
+// columns (two 16-byte loads per row), quantizes those row blocks from registers
+// (row-wise output) and writes them to LDS; after one barrier each lane reads 16-row
+// column pieces back and quantizes TR/64 column blocks.
+constexpr int kTileC = 64;
+constexpr int kColTileRows = 128;  // rows of a column-wise tile
 
-template <bool k46, bool kSR, bool kRHT, bool kRows>
+template <int TR, bool k46, bool kSR, bool kRHT, bool kRows>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
-  // 256 rows x 32 dwords (64 bf16); logical dword q of row r lives at q ^ sw(r),
+  constexpr int kIt = TR / 64;          // rows per lane in the load phase
+  constexpr int kNRB = TR / 16;         // 16-row blocks per tile
+  constexpr int kLanesPerRB = kThreads / kNRB;
+  constexpr int kH = 32 / kLanesPerRB;  // dword columns (column pairs) per lane
+  // TR rows x 32 dwords (64 bf16); logical dword q of row r lives at q ^ sw(r),
   // sw(r) = 4 * ((r >> 4) & 7).
-  __shared__ uint32_t lds[kTileR * 32];
+  __shared__ uint32_t lds[TR * 32];
   const int64_t R = a.rows, C = a.cols;
   const int64_t tiles_c = (C + kTileC - 1) / kTileC;
-  const int64_t R0 = (int64_t)(blockIdx.x / tiles_c) * kTileR;
+  const int64_t R0 = (int64_t)(blockIdx.x / tiles_c) * TR;
   const int64_t C0 = (int64_t)(blockIdx.x % tiles_c) * kTileC;
   const int tid = threadIdx.x;
 
-  // all eight 16-byte loads of the lane are in flight before anything waits on them
+  // all of the lane's 16-byte loads are in flight before anything waits on them
   const int j = tid & 3;
-  uint4 w[8];
+  uint4 w[2 * kIt];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kIt; ++k) {
     const int row = (tid >> 2) + 64 * k;
     const int64_t gr = R0 + row, gc = C0 + 16 * j;
     w[2 * k] = make_uint4(0, 0, 0, 0);
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kIt; ++k) {
     const int row = (tid >> 2) + 64 * k;
     const int64_t gr = R0 + row, gc = C0 + 16 * j;
     const bool ok = gr < R && gc < C;
@@ -145,12 +154,12 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
   }
   __syncthreads();
 
-  const int rb = tid & 15;
+  const int rb = tid % kNRB;
   const int sw = 4 * (rb & 7);
   const int64_t nrb = R / 16;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int p = (tid >> 4) + 16 * h;
+  for (int h = 0; h < kH; ++h) {
+    const int p = tid / kNRB + kLanesPerRB * h;
     const int64_t gr0 = R0 + 16 * rb, gc = C0 + 2 * p;
     if (gr0 >= R || gc >= C) continue;
     float va[16], vb[16];
@@ -262,11 +271,12 @@ hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
     quant_rows_kernel<k46, kSR, kRHT><<<grid, kThreads, 0, s>>>(a, nblk);
     return hipGetLastError();
   }
-  const int64_t grid = ((a.rows + kTileR - 1) / kTileR) * ((a.cols + kTileC - 1) / kTileC);
+  constexpr int TR = kColTileRows;
+  const int64_t grid = ((a.rows + TR - 1) / TR) * ((a.cols + kTileC - 1) / kTileC);
   if (a.rows_out)
-    quant_tile_kernel<k46, kSR, kRHT, true><<<grid, kThreads, 0, s>>>(a);
+    quant_tile_kernel<TR, k46, kSR, kRHT, true><<<grid, kThreads, 0, s>>>(a);
   else
-    quant_tile_kernel<k46, kSR, kRHT, false><<<grid, kThreads, 0, s>>>(a);
+    quant_tile_kernel<TR, k46, kSR, kRHT, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
