@@ -239,7 +239,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
-                    help="profiling aid: run one piece (c2_step, c2_kernel, c5_qlinear, copy) and exit")
+                    help="profiling aid: run one piece (c2_step, c2_kernel, c3_kernel, c4a_kernel, "
+                         "c4b_kernel, c5_qlinear, copy) and exit")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -272,7 +273,14 @@ def main():
             torch.cuda.synchronize()
             log("copy: 268435456 bytes per dispatch")
             return
-        case = QuantCase(fos, x2, {}, 3)
+        kernels = {"c2_kernel": ("c2", {}), "c2_step": ("c2", {}),
+                   "c3_kernel": ("c3", {"outputs": ("row", "col")}),
+                   "c4a_kernel": ("c4a", {"hadamard_seed": 0, "rounding": "sr", "sr_seed": 1234}),
+                   "c4b_kernel": ("c4b", {"block": "2d"})}
+        if args.only not in kernels:
+            raise SystemExit(f"unknown --only {args.only}")
+        name, kw = kernels[args.only]
+        case = QuantCase(fos, x2 if name == "c2" else W.make(name), kw, 3)
         fn = case.step if args.only == "c2_step" else case.scaled
         case.step(0); case.step(1); case.step(2)
         for i in range(args.steps):

@@ -184,68 +184,99 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
 }
 
 // ------------------------------------------------------------------ 2D 16x16 tiles
+// Reductions over the 16 lanes of a DPP row, every lane receiving the result.  The
+// partners are lane ^ 1, lane ^ 2 (quad permutes), then the mirrored lane of the other
+// quad (row_half_mirror) and of the other half row (row_mirror); for the sum this is
+// the pairwise order ((p0 + p1) + (p2 + p3)) + ... up to commutativity of each add.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_f32<0xB1>(v);
+  v = v + dpp_f32<0x4E>(v);
+  v = v + dpp_f32<0x141>(v);
+  return v + dpp_f32<0x140>(v);
+}
+
+// A workgroup covers two vertically adjacent rows of 16 tiles; the 16 lanes of a DPP
+// row hold the 16 rows of one tile (one 16-value row block each), for both tile rows.
+constexpr int k2dTileRows = 2;
+
 template <bool k46, bool kSR, bool kRows, bool kCols>
 __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
-  __shared__ uint2 tr[16][17];
+  __shared__ uint2 tr[k2dTileRows][16][17];
   const int64_t R = a.rows, C = a.cols;
-  const int64_t tiles_c = C / 16;
-  const int64_t wg_per_row = (tiles_c + 15) / 16;
-  const int64_t R0 = (int64_t)(blockIdx.x / wg_per_row) * 16;
+  const uint32_t tiles_c = (uint32_t)(C / 16);
+  const uint32_t wg_per_row = (tiles_c + 15) / 16;
+  const int64_t R0 = (int64_t)(blockIdx.x / wg_per_row) * (16 * k2dTileRows);
   const int tid = threadIdx.x;
   const int row = tid & 15, tl = tid >> 4;
-  const int64_t T = (int64_t)(blockIdx.x % wg_per_row) * 16 + tl;
+  const uint32_t T = (blockIdx.x % wg_per_row) * 16 + tl;
   const bool valid = T < tiles_c;
 
-  uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-  if (valid) {
-    const uint4* p = reinterpret_cast<const uint4*>(a.x + (R0 + row) * C + 16 * T);
-    w0 = p[0];
-    w1 = p[1];
+  uint4 w[2 * k2dTileRows];
+#pragma unroll
+  for (int q = 0; q < k2dTileRows; ++q) {
+    w[2 * q] = make_uint4(0, 0, 0, 0);
+    w[2 * q + 1] = w[2 * q];
+    if (valid && R0 + 16 * q < R) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.x + (R0 + 16 * q + row) * C + 16 * T);
+      w[2 * q] = p[0];
+      w[2 * q + 1] = p[1];
+    }
   }
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab);
-  float v[16];
-  unpack16(w0, w1, v);
-  float srq[16];
-  const int64_t rblk = (R0 + row) * tiles_c + T;    // row-wise block id of this row
-  if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srq);
 
-  float am = amax16(v);
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+  for (int q = 0; q < k2dTileRows; ++q) {
+    const int64_t Rq = R0 + 16 * q;
+    if (Rq >= R) break;                         // uniform across the workgroup
+    float v[16];
+    unpack16(w[2 * q], w[2 * q + 1], v);
+    float srq[16];
+    const int64_t rblk = (Rq + row) * tiles_c + T;    // row-wise block id of this row
+    if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srq);
 
-  Cand c6, c4;
-  float inv6, inv4;
-  cand_scale(am, tc.u6, tc.tab, c6.s, c6.d, inv6);
-  if (kSR) cand_codes_sr(v, c6.d, inv6, srq, c6); else cand_codes_rne(v, c6.d, inv6, c6);
+    const float am = row16_max(amax16(v));
+    Cand c6, c4;
+    float inv6, inv4;
+    cand_scale(am, tc.u6, tc.tab, c6.s, c6.d, inv6);
+    if (kSR) cand_codes_sr(v, c6.d, inv6, srq, c6); else cand_codes_rne(v, c6.d, inv6, c6);
+    c6.err = row16_sum(c6.err);
+    Cand c = c6;
+    if (k46) {
+      cand_scale(am, tc.u4, tc.tab, c4.s, c4.d, inv4);
+      if (kSR) cand_codes_sr(v, c4.d, inv4, srq, c4); else cand_codes_rne(v, c4.d, inv4, c4);
+      c4.err = row16_sum(c4.err);
+      if (c4.err < c6.err) c = c4;
+    }
+    if (kRows && valid) store_block(a.row_data, a.row_scales, 8 * rblk, rblk, c);
+    if (kCols) {
+      tr[q][tl][row] = make_uint2(c.lo, c.hi);
+      __syncthreads();
+      if (valid) {
+        const int cc = row;                      // this lane now owns column cc of the tile
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) c6.err = c6.err + __shfl_xor(c6.err, m);
-  Cand c = c6;
-  if (k46) {
-    cand_scale(am, tc.u4, tc.tab, c4.s, c4.d, inv4);
-    if (kSR) cand_codes_sr(v, c4.d, inv4, srq, c4); else cand_codes_rne(v, c4.d, inv4, c4);
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) c4.err = c4.err + __shfl_xor(c4.err, m);
-    if (c4.err < c6.err) c = c4;
-  }
-  if (kRows && valid) store_block(a.row_data, a.row_scales, 8 * rblk, rblk, c);
-  if (kCols) {
-    tr[tl][row] = make_uint2(c.lo, c.hi);
-    __syncthreads();
-    if (valid) {
-      const int cc = row;                      // this lane now owns column cc of the tile
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint2 q = tr[tl][i];
-        const uint32_t word = (cc < 8) ? q.x : q.y;
-        const uint32_t nib = (word >> (4 * (cc & 7))) & 0xfu;
-        if (i < 8) lo |= nib << (4 * i); else hi |= nib << (4 * (i - 8));
+        for (int i = 0; i < 16; ++i) {
+          const uint2 qq = tr[q][tl][i];
+          const uint32_t word = (cc < 8) ? qq.x : qq.y;
+          const uint32_t nib = (word >> (4 * (cc & 7))) & 0xfu;
+          if (i < 8) lo |= nib << (4 * i); else hi |= nib << (4 * (i - 8));
+        }
+        const int64_t col = 16 * (int64_t)T + cc;
+        const int64_t cblk = col * (R / 16) + Rq / 16;
+        *reinterpret_cast<uint2*>(a.col_data + 8 * cblk) = make_uint2(lo, hi);
+        a.col_scales[cblk] = (uint8_t)c.s;
       }
-      const int64_t col = 16 * T + cc;
-      const int64_t cblk = col * (R / 16) + R0 / 16;
-      *reinterpret_cast<uint2*>(a.col_data + 8 * cblk) = make_uint2(lo, hi);
-      a.col_scales[cblk] = (uint8_t)c.s;
     }
   }
 }
@@ -253,7 +284,8 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
 template <bool k46, bool kSR>
 hipError_t dispatch_2d(const QuantArgs& a, hipStream_t s) {
   const int64_t tiles_c = a.cols / 16;
-  const int64_t grid = (a.rows / 16) * ((tiles_c + 15) / 16);
+  const int64_t tile_rows = a.rows / 16;
+  const int64_t grid = ((tile_rows + k2dTileRows - 1) / k2dTileRows) * ((tiles_c + 15) / 16);
   if (a.rows_out && a.cols_out)
     quant_2d_kernel<k46, kSR, true, true><<<grid, kThreads, 0, s>>>(a);
   else if (a.rows_out)
