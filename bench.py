@@ -194,6 +194,29 @@ def bench_qlinear(fos, x_cpu, w_cpu, steps, warmup):
             "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
 
 
+def bench_qlinear_bwd(fos, x_cpu, w_cpu, dy_cpu, steps, warmup):
+    """Backward products of the c5 layer: dX = deq(dY) deq(W^T)^T (inner 12288) and
+    dW = deq(dY^T) deq(X^T)^T (inner 8192), from training-style records: dY row and
+    column-wise with stochastic rounding, X column-wise, W column-wise in 2D blocks."""
+    import torch
+    dev = "cuda:0"
+    gq, gqt = fos.quantize(dy_cpu.to(dev), outputs=("row", "col"), rounding="sr", sr_seed=1234)
+    xqt = fos.quantize(x_cpu.to(dev), outputs=("col",))
+    wqt = fos.quantize(w_cpu.to(dev), outputs=("col",), block="2d")
+    M, N = gq.shape
+    K = xqt.shape[0]
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    trip = lambda q: (q.data, q.scales, q.tensor_scale)
+
+    def fn(i):
+        fos.fos_qlinear_bwd(trip(gq), trip(gqt), trip(xqt), trip(wqt), M, N, K, dx, dw)
+    ms = time_loop(fn, max(10, steps // 2), max(15, warmup), 1)
+    flops = 2 * (2 * M * N * K)
+    return {"shapes": {"dX": [M, K, N], "dW": [N, K, M]}, "flop": flops, "ms": ms,
+            "TFLOPs": flops / ms / 1e9, "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+
+
 def copy_reference(steps):
     """A plain device-to-device copy (torch's copy kernel) of 256 MiB: a measured
     ceiling for streaming read+write traffic on this GPU."""
@@ -314,6 +337,10 @@ def main():
     log("C5 qlinear ...")
     rows["c5_qlinear"] = bench_qlinear(fos, W.make("c5_x"), W.make("c5_w"), args.steps, args.warmup)
     log(json.dumps(rows["c5_qlinear"]))
+    log("C5 qlinear backward ...")
+    rows["c5_qlinear_bwd"] = bench_qlinear_bwd(fos, W.make("c5_x"), W.make("c5_w"),
+                                               W.make("c5_dy"), args.steps, args.warmup)
+    log(json.dumps(rows["c5_qlinear_bwd"]))
 
     cpu = None
     if not args.no_cpu:

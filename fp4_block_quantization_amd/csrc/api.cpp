@@ -122,6 +122,33 @@ fos_status launch_scale(const fos_quant_config* cfg, const void* x, int64_t rows
   return e == hipSuccess ? FOS_OK : FOS_E_HIP;
 }
 
+// Y[M][N] = deq(A) deq(B)^T for records A [M][K], B [N][K] blocked along K.
+fos_status check_gemm(const uint8_t* a_data, const uint8_t* a_scales, const float* a_t,
+                      const uint8_t* b_data, const uint8_t* b_scales, const float* b_t,
+                      int64_t M, int64_t N, int64_t K, const void* y) {
+  if (M < 1 || N < 1 || K < 64 || K % 64 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return FOS_E_SHAPE;
+  if (N > kMaxElems / M || K > kMaxElems / M || K > kMaxElems / N) return FOS_E_SHAPE;
+  // each packed operand is addressed through one buffer resource (< 4 GiB)
+  if ((M + 256) * (K / 2) >= ((int64_t)1 << 32) || (N + 256) * (K / 2) >= ((int64_t)1 << 32))
+    return FOS_E_SHAPE;
+  if (!a_data || !a_scales || !a_t || !b_data || !b_scales || !b_t || !y) return FOS_E_NULL;
+  if (!aligned(a_data, 16) || !aligned(b_data, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(y, 2) || !aligned(a_t, 4) || !aligned(b_t, 4))
+    return FOS_E_ALIGN;
+  return FOS_OK;
+}
+
+fos_status launch_gemm(const uint8_t* a_data, const uint8_t* a_scales, const float* a_t,
+                       const uint8_t* b_data, const uint8_t* b_scales, const float* b_t,
+                       int64_t M, int64_t N, int64_t K, void* y, void* stream) {
+  return fos::launch_qlinear(a_data, a_scales, a_t, b_data, b_scales, b_t, M, N, K,
+                             static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,24 +245,37 @@ fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
                            const float* x_tensor_scale, const uint8_t* w_data,
                            const uint8_t* w_scales, const float* w_tensor_scale, int64_t M,
                            int64_t N, int64_t K, void* y_bf16, void* stream) {
-  if (M < 1 || N < 1 || K < 64 || K % 64 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
-    return FOS_E_SHAPE;
-  if (N > kMaxElems / M || K > kMaxElems / M || K > kMaxElems / N) return FOS_E_SHAPE;
-  // each packed operand is addressed through one buffer resource (< 4 GiB)
-  if ((M + 256) * (K / 2) >= ((int64_t)1 << 32) || (N + 256) * (K / 2) >= ((int64_t)1 << 32))
-    return FOS_E_SHAPE;
-  if (!x_data || !x_scales || !x_tensor_scale || !w_data || !w_scales || !w_tensor_scale ||
-      !y_bf16)
-    return FOS_E_NULL;
-  if (!aligned(x_data, 16) || !aligned(w_data, 16) || !aligned(x_scales, 4) ||
-      !aligned(w_scales, 4) || !aligned(y_bf16, 2) || !aligned(x_tensor_scale, 4) ||
-      !aligned(w_tensor_scale, 4))
-    return FOS_E_ALIGN;
-  return fos::launch_qlinear(x_data, x_scales, x_tensor_scale, w_data, w_scales, w_tensor_scale,
-                             M, N, K, static_cast<uint16_t*>(y_bf16),
-                             static_cast<hipStream_t>(stream)) == hipSuccess
-             ? FOS_OK
-             : FOS_E_HIP;
+  const fos_status st = check_gemm(x_data, x_scales, x_tensor_scale, w_data, w_scales,
+                                   w_tensor_scale, M, N, K, y_bf16);
+  if (st != FOS_OK) return st;
+  return launch_gemm(x_data, x_scales, x_tensor_scale, w_data, w_scales, w_tensor_scale, M, N, K,
+                     y_bf16, stream);
+}
+
+fos_status fos_qlinear_bwd(const uint8_t* dy_data, const uint8_t* dy_scales,
+                           const float* dy_tensor_scale, const uint8_t* dyt_data,
+                           const uint8_t* dyt_scales, const float* dyt_tensor_scale,
+                           const uint8_t* xt_data, const uint8_t* xt_scales,
+                           const float* xt_tensor_scale, const uint8_t* wt_data,
+                           const uint8_t* wt_scales, const float* wt_tensor_scale, int64_t M,
+                           int64_t N, int64_t K, void* dx_bf16, void* dw_bf16, void* stream) {
+  if (!dx_bf16 && !dw_bf16) return FOS_E_NULL;
+  fos_status st;
+  // dX [M][K] = deq(dY) deq(W^T)^T: inner dimension N
+  if (dx_bf16 && (st = check_gemm(dy_data, dy_scales, dy_tensor_scale, wt_data, wt_scales,
+                                  wt_tensor_scale, M, K, N, dx_bf16)) != FOS_OK)
+    return st;
+  // dW [N][K] = deq(dY^T) deq(X^T)^T: inner dimension M
+  if (dw_bf16 && (st = check_gemm(dyt_data, dyt_scales, dyt_tensor_scale, xt_data, xt_scales,
+                                  xt_tensor_scale, N, K, M, dw_bf16)) != FOS_OK)
+    return st;
+  if (dx_bf16 && (st = launch_gemm(dy_data, dy_scales, dy_tensor_scale, wt_data, wt_scales,
+                                   wt_tensor_scale, M, K, N, dx_bf16, stream)) != FOS_OK)
+    return st;
+  if (dw_bf16)
+    return launch_gemm(dyt_data, dyt_scales, dyt_tensor_scale, xt_data, xt_scales,
+                       xt_tensor_scale, N, K, M, dw_bf16, stream);
+  return FOS_OK;
 }
 
 }  // extern "C"

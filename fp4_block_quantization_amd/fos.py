@@ -56,6 +56,7 @@ def _load() -> ctypes.CDLL:
         "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_qlinear_fwd": ([P, P, P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
+        "fos_qlinear_bwd": ([P] * 12 + [I64, I64, I64, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -161,6 +162,17 @@ def fos_qlinear_fwd(x_data, x_scales, x_t, w_data, w_scales, w_t, M: int, N: int
            "fos_qlinear_fwd")
 
 
+def fos_qlinear_bwd(dy, dyt, xt, wt, M: int, N: int, K: int, dx: Optional[torch.Tensor],
+                    dw: Optional[torch.Tensor]) -> None:
+    """dy, dyt, xt, wt: (data, scales, tensor_scale) triples (a skipped product's
+    operands may be None)."""
+    def trip(r):
+        return [_ptr(v) for v in r] if r is not None else [_ptr(None)] * 3
+    dev = (dx if dx is not None else dw).device
+    _check(_lib.fos_qlinear_bwd(*trip(dy), *trip(dyt), *trip(xt), *trip(wt), M, N, K, _ptr(dx),
+                                _ptr(dw), _stream(dev)), "fos_qlinear_bwd")
+
+
 # ---------------------------------------------------------------- tensor-level API
 
 @dataclass
@@ -249,3 +261,37 @@ def qlinear_fwd(xq: NVFP4Tensor, wq: NVFP4Tensor, out: Optional[torch.Tensor] = 
     fos_qlinear_fwd(xq.data, xq.scales, xq.tensor_scale, wq.data, wq.scales, wq.tensor_scale,
                     M, N, K, y)
     return y
+
+
+def qlinear_bwd(dyq: Optional[NVFP4Tensor], dyq_t: Optional[NVFP4Tensor],
+                xq_t: Optional[NVFP4Tensor], wq_t: Optional[NVFP4Tensor],
+                need_dx: bool = True, need_dw: bool = True
+                ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Backward of Y = X W^T from NVFP4 records: dX = deq(dY) deq(W^T)^T and
+    dW = deq(dY^T) deq(X^T)^T (bf16).  dyq: row-wise record of dY [M, N]; dyq_t,
+    xq_t, wq_t: column-wise records of dY, X and W (records of dY^T [N, M], X^T [K, M],
+    W^T [K, N])."""
+    if not (need_dx or need_dw):
+        raise ValueError("nothing to compute")
+    if need_dx:
+        M, N = dyq.shape
+        K, N2 = wq_t.shape
+        if N2 != N:
+            raise ValueError("dY and W disagree on N")
+    if need_dw:
+        N3, M3 = dyq_t.shape
+        K3, M4 = xq_t.shape
+        if M3 != M4:
+            raise ValueError("dY and X disagree on M")
+        if need_dx and (N3 != N or M3 != M or K3 != K):
+            raise ValueError("inconsistent shapes")
+        M, N, K = M3, N3, K3
+    ref = dyq if need_dx else dyq_t
+    dev = ref.data.device
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev) if need_dx else None
+    dw = torch.empty(N, K, dtype=torch.bfloat16, device=dev) if need_dw else None
+    trip = lambda q: (q.data, q.scales, q.tensor_scale) if q is not None else None
+    fos_qlinear_bwd(trip(dyq) if need_dx else None, trip(dyq_t) if need_dw else None,
+                    trip(xq_t) if need_dw else None, trip(wq_t) if need_dx else None,
+                    M, N, K, dx, dw)
+    return dx, dw

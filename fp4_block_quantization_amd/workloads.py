@@ -19,6 +19,8 @@ not used):
   c4a           8192x4096 bf16 gradient, N(0, 1e-3).
   c4b           12288x4096 bf16 weight, N(0, 0.02).
   c5_x, c5_w    qlinear operands: X 8192x4096 Student-t(nu=3), W 12288x4096 N(0, 0.02).
+  c5_dy         output gradient of that layer for the backward products: 8192x12288
+                N(0, 1e-3) (the gradient recipe of c4a).
 """
 from __future__ import annotations
 
@@ -39,6 +41,7 @@ SHAPES = {
     "c4b": (12288, 4096),
     "c5_x": (8192, 4096),
     "c5_w": (12288, 4096),
+    "c5_dy": (8192, 12288),
 }
 
 
@@ -82,6 +85,9 @@ def make(name: str) -> torch.Tensor:
     elif name == "c5_w":
         g = torch.Generator().manual_seed(7)
         x = 0.02 * torch.randn(*shape, generator=g)
+    elif name == "c5_dy":
+        g = torch.Generator().manual_seed(8)
+        x = 1e-3 * torch.randn(*shape, generator=g)
     else:  # pragma: no cover - guarded by SHAPES lookup
         raise KeyError(name)
     return x.to(torch.bfloat16).contiguous()

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FOS_ABI_VERSION 1
+#define FOS_ABI_VERSION 2
 
 typedef enum {
   FOS_OK = 0,
@@ -152,8 +152,10 @@ fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales,
  * Six": without native FP4 matmuls the layer is simulated with a higher-precision
  * matrix multiplication of the dequantized operands):
  *   Y[m][n] = bf16( (t_x * t_w) * sum_k (E*D)_x[m][k] * (E*D)_w[n][k] )
- * Operands are row-wise NVFP4 records blocked along K: Xq [M][K] (x_data
- * [M][K/2], x_scales [M][K/16]) and Wq [N][K] (the [out][in] Linear layout).
+ * Operands are NVFP4 records blocked along K: Xq [M][K] (x_data [M][K/2],
+ * x_scales [M][K/16]) and Wq [N][K] (the [out][in] Linear layout); any records
+ * blocked along their shared dimension work (e.g. column-wise records, which are
+ * the records of the transposes, or 2D records).
  * E*D products are formed exactly in fp16, multiplied on the matrix cores with fp32
  * accumulation; the tensor scales are applied in fp32 before the bf16 rounding.
  *   M, N >= 1; K >= 64 and K % 64 == 0; (M + 256) * K / 2 and (N + 256) * K / 2
@@ -165,6 +167,33 @@ fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
                            const float* x_tensor_scale, const uint8_t* w_data,
                            const uint8_t* w_scales, const float* w_tensor_scale,
                            int64_t M, int64_t N, int64_t K, void* y_bf16, void* stream);
+
+/* Backward pass of the simulated quantized linear layer (Four Over Six documentation
+ * page, "Training": the quantized linear layer implements a backward pass).  For
+ * Y = X W^T with X [M][K], W [N][K] and the output gradient dY [M][N]:
+ *   dX [M][K] = bf16( deq(dY) . deq(W^T)^T )      inner dimension N
+ *   dW [N][K] = bf16( deq(dY^T) . deq(X^T)^T )    inner dimension M
+ * computed by the same kernel as fos_qlinear_fwd, from records blocked along each
+ * product's inner dimension:
+ *   dy_*  : row-wise record of dY   [M][N]   (blocked along N)
+ *   dyt_* : column-wise record of dY = record of dY^T [N][M]   (blocked along M)
+ *   xt_*  : column-wise record of X  = record of X^T  [K][M]   (blocked along M)
+ *   wt_*  : column-wise record of W  = record of W^T  [K][N]   (blocked along N)
+ * A random Hadamard transform on the two operands of one product with the same seed
+ * (e.g. dY^T and X^T along M) cancels in the product, since the transform is
+ * orthogonal.  dx_bf16 or dw_bf16 may be NULL to skip that product (not both);
+ * the operands of a skipped product are not read.  Shapes and alignment as for
+ * fos_qlinear_fwd, with each product's inner dimension in the role of K.  All
+ * arguments are validated before either product is launched.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_qlinear_bwd(const uint8_t* dy_data, const uint8_t* dy_scales,
+                           const float* dy_tensor_scale, const uint8_t* dyt_data,
+                           const uint8_t* dyt_scales, const float* dyt_tensor_scale,
+                           const uint8_t* xt_data, const uint8_t* xt_scales,
+                           const float* xt_tensor_scale, const uint8_t* wt_data,
+                           const uint8_t* wt_scales, const float* wt_tensor_scale,
+                           int64_t M, int64_t N, int64_t K, void* dx_bf16, void* dw_bf16,
+                           void* stream);
 
 #ifdef __cplusplus
 }

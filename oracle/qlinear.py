@@ -12,6 +12,11 @@ per-tensor scales are applied after the dot product:
     Y64[m, n] = t_x * t_w * sum_k (E*D)_x[m, k] * (E*D)_w[n, k]
 Operands are in the row-wise layout, blocked along K: Xq [M, K], Wq [N, K] (the
 PyTorch Linear weight layout [out, in]).
+
+Backward (§Training: the quantized linear layer implements its backward pass): for
+Y = X W^T and output gradient dY [M, N], dX = dY W and dW = dY^T X.  Each product is
+formed from records blocked along its own inner dimension, which for W^T, dY^T and
+X^T are the column-wise records (the quantizations of the transposes).
 """
 from __future__ import annotations
 
@@ -40,3 +45,15 @@ def qlinear_ref64(x_data, x_scales, x_t, w_data, w_scales, w_t,
     ax = operand_exact(x_data, x_scales, rows)
     bw = operand_exact(w_data, w_scales, cols)
     return (float(x_t) * float(w_t)) * (ax @ bw.T)
+
+
+def qlinear_bwd_ref64(dy=None, dyt=None, xt=None, wt=None):
+    """fp64 references of the backward products.  Each argument is a record as a
+    (data, scales, t) triple:
+      dy : row-wise record of dY [M, N];      wt : record of W^T [K, N]
+      dyt: record of dY^T [N, M];             xt : record of X^T [K, M]
+    Returns (dX [M, K] = deq(dY) deq(W^T)^T, dW [N, K] = deq(dY^T) deq(X^T)^T); a
+    product whose operands are missing is None."""
+    dx = qlinear_ref64(*dy, *wt) if dy is not None and wt is not None else None
+    dw = qlinear_ref64(*dyt, *xt) if dyt is not None and xt is not None else None
+    return dx, dw

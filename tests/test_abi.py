@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert fos.ABI_VERSION == 1
+    assert fos.ABI_VERSION == 2
     for s in range(7):
         assert fos.lib().fos_status_string(s).startswith(b"FOS_")
     assert fos.lib().fos_workspace_bytes() >= 8
@@ -103,6 +103,25 @@ def test_qlinear_validation():
     assert L.fos_qlinear_fwd(MIS, f, f, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_ALIGN
     # a packed operand must fit one buffer resource (< 4 GiB)
     assert L.fos_qlinear_fwd(f, f, f, f, f, f, 1 << 20, 256, 1 << 13, f, None) == fos.FOS_E_SHAPE
+
+
+def test_qlinear_bwd_validation():
+    """All arguments are checked before either product launches; a skipped product's
+    operands may be NULL."""
+    L = fos.lib()
+    f, z = FAKE, None
+    ok3, no3 = [f, f, f], [z, z, z]
+    # nothing requested
+    assert L.fos_qlinear_bwd(*ok3, *ok3, *ok3, *ok3, 256, 256, 256, z, z, z) == fos.FOS_E_NULL
+    # dX's inner dimension is N, dW's is M
+    assert L.fos_qlinear_bwd(*ok3, *ok3, *ok3, *ok3, 256, 100, 256, f, z, z) == fos.FOS_E_SHAPE
+    assert L.fos_qlinear_bwd(*ok3, *ok3, *ok3, *ok3, 100, 256, 256, z, f, z) == fos.FOS_E_SHAPE
+    # a bad dW request fails validation even though dX alone would be fine
+    assert L.fos_qlinear_bwd(*ok3, *ok3, *ok3, *ok3, 100, 256, 256, f, f, z) == fos.FOS_E_SHAPE
+    # operands of the product that is computed must be present
+    assert L.fos_qlinear_bwd(*ok3, *no3, *no3, *no3, 256, 256, 256, f, z, z) == fos.FOS_E_NULL
+    assert L.fos_qlinear_bwd(*no3, *ok3, *no3, *no3, 256, 256, 256, z, f, z) == fos.FOS_E_NULL
+    assert L.fos_qlinear_bwd(*ok3, *ok3, *ok3, MIS, f, f, 256, 256, 256, f, f, z) == fos.FOS_E_ALIGN
 
 
 def test_tensor_scale_validation():

@@ -374,3 +374,60 @@ def test_qlinear_full_size_c5_sampled(fos, workloads):
     ref16 = F.bf16_bits_to_f32(F.f32_to_bf16_bits(y64.astype(np.float32))).astype(np.float64)
     rel = np.linalg.norm(yg - ref16) / np.linalg.norm(y64)
     assert rel <= 1e-3, rel
+
+
+# ------------------------------------------------------------------ qlinear backward
+
+def _dev_record(fos, o, lay):
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    t = torch.tensor([o["t"]], dtype=torch.float32, device=DEV)
+    return fos.NVFP4Tensor(dev(o[f"{lay}_data"]), dev(o[f"{lay}_scales"]), t, lay)
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 768, 320), (192, 320, 128), (256, 256, 256),
+                                   (320, 1088, 64)])
+def test_qlinear_bwd_matches_fp64_reference(fos, m, n, k):
+    """dX = deq(dY) deq(W^T)^T and dW = deq(dY^T) deq(X^T)^T from the oracle's records
+    (dY with stochastic rounding, W with 2D blocks, as in training)."""
+    xb = bits_of(W.random_bf16(m, k, 3 * m + k, "student_t"))
+    wb = bits_of(W.random_bf16(n, k, n + 5 * k, "normal", scale=0.02))
+    gb = bits_of(W.random_bf16(m, n, m + 7 * n, "normal", scale=1e-3))
+    ox = N.quantize(xb, N.Config(cols_out=True))
+    ow = N.quantize(wb, N.Config(cols_out=True, block="2d"))
+    og = N.quantize(gb, N.Config(cols_out=True, rounding="sr", sr_seed=77))
+    dx, dw = fos.qlinear_bwd(_dev_record(fos, og, "row"), _dev_record(fos, og, "col"),
+                             _dev_record(fos, ox, "col"), _dev_record(fos, ow, "col"))
+    assert dx.shape == (m, k) and dw.shape == (n, k)
+    _qlinear_check(bits_of(dx.cpu()), og["row_data"], og["row_scales"], og["t"],
+                   ow["col_data"], ow["col_scales"], ow["t"])
+    _qlinear_check(bits_of(dw.cpu()), og["col_data"], og["col_scales"], og["t"],
+                   ox["col_data"], ox["col_scales"], ox["t"])
+    # either product alone
+    dx2, none = fos.qlinear_bwd(_dev_record(fos, og, "row"), None, None,
+                                _dev_record(fos, ow, "col"), need_dw=False)
+    assert none is None and torch.equal(dx2, dx)
+    none, dw2 = fos.qlinear_bwd(None, _dev_record(fos, og, "col"), _dev_record(fos, ox, "col"),
+                                None, need_dx=False)
+    assert none is None and torch.equal(dw2, dw)
+
+
+def test_qlinear_bwd_end_to_end_with_hadamard(fos):
+    """Training-step records quantized on the GPU: dY^T and X^T column-wise with the
+    same Hadamard seed and stochastic rounding; dW against the oracle's records."""
+    m, n, k = 512, 256, 384
+    xb = bits_of(W.random_bf16(m, k, 41, "student_t"))
+    gb = bits_of(W.random_bf16(m, n, 43, "normal", scale=1e-3))
+    cfg_x = N.Config(rows_out=False, cols_out=True, hadamard=True, hadamard_seed=9)
+    cfg_g = N.Config(rows_out=False, cols_out=True, hadamard=True, hadamard_seed=9,
+                     rounding="sr", sr_seed=5)
+    gx = fos.quantize(to_gpu_bf16(xb), outputs=("col",), hadamard_seed=9)
+    gg = fos.quantize(to_gpu_bf16(gb), outputs=("col",), hadamard_seed=9, rounding="sr",
+                      sr_seed=5)
+    _, dw = fos.qlinear_bwd(None, gg, gx, None, need_dx=False)
+    ox, og = N.quantize(xb, cfg_x), N.quantize(gb, cfg_g)
+    _qlinear_check(bits_of(dw.cpu()), og["col_data"], og["col_scales"], og["t"],
+                   ox["col_data"], ox["col_scales"], ox["t"])
+    # the transform cancels: dW approximates dY^T X of the unquantized tensors
+    exact = F.bf16_bits_to_f32(gb).astype(np.float64).T @ F.bf16_bits_to_f32(xb).astype(np.float64)
+    got = F.bf16_bits_to_f32(bits_of(dw.cpu())).astype(np.float64)
+    assert np.linalg.norm(got - exact) / np.linalg.norm(exact) < 0.15
