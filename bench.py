@@ -174,6 +174,33 @@ def bench_dequant(fos, x_cpu, steps, warmup):
     return rows
 
 
+def bench_dequant_hadamard(fos, x_cpu, steps, warmup):
+    """Dequantize + inverse Hadamard transform of the c4a record (bf16 out)."""
+    import ctypes
+    import torch
+    R, C = x_cpu.shape
+    dev = "cuda:0"
+    q = fos.quantize(x_cpu.to(dev), hadamard_seed=0, rounding="sr", sr_seed=1234)
+    lib = fos.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    sets = 3
+    outs = [torch.empty(R, C, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    datas = [q.data.clone() for _ in range(sets)]
+    scs = [q.scales.clone() for _ in range(sets)]
+    args = [(_vp(datas[i]), _vp(scs[i]), _vp(q.tensor_scale), R, C, 0, fos.FOS_OUT_BF16,
+             _vp(outs[i]), stream) for i in range(sets)]
+    f = lib.fos_dequantize_hadamard
+    bad = [0]
+
+    def fn(i):
+        bad[0] |= f(*args[i])
+    ms = time_loop(fn, steps, warmup, sets)
+    if bad[0]:
+        raise RuntimeError("fos_dequantize_hadamard returned an error status")
+    b = R * C // 2 + R * C // 16 + 4 + 2 * R * C
+    return {"bytes": b, "ms": ms, "GBps": b / ms / 1e6, "frac": b / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def bench_qlinear(fos, x_cpu, w_cpu, steps, warmup):
     import torch
     dev = "cuda:0"
@@ -329,6 +356,9 @@ def main():
     rows["c4a_rht_sr"] = bench_quant(fos, "c4a gradient 8192x4096, Hadamard + stochastic rounding",
                                      W.make("c4a"), {"hadamard_seed": 0, "rounding": "sr",
                                                      "sr_seed": 1234}, args.steps, args.warmup)
+    log("C4a inverse-Hadamard dequantize ...")
+    rows["c4a_dequantize_hadamard_bf16"] = bench_dequant_hadamard(fos, W.make("c4a"), args.steps,
+                                                                  args.warmup)
     log("C4b ...")
     rows["c4b_2d"] = bench_quant(fos, "c4b weight 12288x4096, 2D 16x16", W.make("c4b"),
                                  {"block": "2d"}, args.steps, args.warmup)

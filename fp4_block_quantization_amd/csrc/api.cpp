@@ -149,6 +149,18 @@ fos_status launch_gemm(const uint8_t* a_data, const uint8_t* a_scales, const flo
              : FOS_E_HIP;
 }
 
+fos_status check_dequantize(const uint8_t* data, const uint8_t* scales, const float* tensor_scale,
+                            int64_t rows, int64_t cols, int out_dtype, const void* out) {
+  if (out_dtype != FOS_OUT_F32 && out_dtype != FOS_OUT_BF16) return FOS_E_FLAGS;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
+  if (cols % 16) return FOS_E_SHAPE;
+  if (rows * cols == 0) return FOS_OK;
+  if (!data || !scales || !tensor_scale || !out) return FOS_E_NULL;
+  if (!aligned(data, 8) || !aligned(out, 16) || !aligned(tensor_scale, 4)) return FOS_E_ALIGN;
+  return FOS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,15 +240,23 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
 
 fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales, const float* tensor_scale,
                           int64_t rows, int64_t cols, int out_dtype, void* out, void* stream) {
-  if (out_dtype != FOS_OUT_F32 && out_dtype != FOS_OUT_BF16) return FOS_E_FLAGS;
-  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
-  if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
-  if (cols % 16) return FOS_E_SHAPE;
-  if (rows * cols == 0) return FOS_OK;
-  if (!data || !scales || !tensor_scale || !out) return FOS_E_NULL;
-  if (!aligned(data, 8) || !aligned(out, 16) || !aligned(tensor_scale, 4)) return FOS_E_ALIGN;
+  const fos_status st = check_dequantize(data, scales, tensor_scale, rows, cols, out_dtype, out);
+  if (st != FOS_OK || rows * cols == 0) return st;
   return fos::launch_dequantize(data, scales, tensor_scale, rows, cols, out_dtype == FOS_OUT_BF16,
                                 out, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
+fos_status fos_dequantize_hadamard(const uint8_t* data, const uint8_t* scales,
+                                   const float* tensor_scale, int64_t rows, int64_t cols,
+                                   uint64_t hadamard_seed, int out_dtype, void* out,
+                                   void* stream) {
+  const fos_status st = check_dequantize(data, scales, tensor_scale, rows, cols, out_dtype, out);
+  if (st != FOS_OK || rows * cols == 0) return st;
+  return fos::launch_dequantize_hadamard(data, scales, tensor_scale, rows, cols,
+                                         hadamard_mask(hadamard_seed), out_dtype == FOS_OUT_BF16,
+                                         out, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FOS_OK
              : FOS_E_HIP;
 }

@@ -58,7 +58,68 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   for (; g < nchunk; g += stride) dequant_chunk<kBF16>(data, scales, t, g, out);
 }
 
+// Records made with the random Hadamard transform, returned to the original basis:
+// lane = one 16-value block (8 nibble bytes + 1 scale byte in, 32 or 64 bytes out);
+// values are dequantized exactly as above, then inverse-transformed in registers.
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads) void dequant_rht_kernel(const uint2* __restrict__ data,
+                                                               const uint8_t* __restrict__ scales,
+                                                               const float* __restrict__ tscale,
+                                                               int64_t nblk, uint32_t mask,
+                                                               void* __restrict__ out) {
+  const float t = tscale[0];
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+    const uint2 q = data[b];
+    const float d = e4m3_decode(scales[b]) * t;
+    const f32x2 e[8] = {cvt_pk_f32_fp4<0>(q.x), cvt_pk_f32_fp4<1>(q.x), cvt_pk_f32_fp4<2>(q.x),
+                        cvt_pk_f32_fp4<3>(q.x), cvt_pk_f32_fp4<0>(q.y), cvt_pk_f32_fp4<1>(q.y),
+                        cvt_pk_f32_fp4<2>(q.y), cvt_pk_f32_fp4<3>(q.y)};
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = e[j].x * d;
+      v[2 * j + 1] = e[j].y * d;
+    }
+    irht16(v, mask);
+    if (kBF16) {
+      uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4 w;
+        w.x = f32_to_bf16_rne(v[8 * h + 0]) | (f32_to_bf16_rne(v[8 * h + 1]) << 16);
+        w.y = f32_to_bf16_rne(v[8 * h + 2]) | (f32_to_bf16_rne(v[8 * h + 3]) << 16);
+        w.z = f32_to_bf16_rne(v[8 * h + 4]) | (f32_to_bf16_rne(v[8 * h + 5]) << 16);
+        w.w = f32_to_bf16_rne(v[8 * h + 6]) | (f32_to_bf16_rne(v[8 * h + 7]) << 16);
+        o[h] = w;
+      }
+    } else {
+      float4* o = reinterpret_cast<float4*>(out) + 4 * b;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o[h] = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dequantize_hadamard(const uint8_t* data, const uint8_t* scales,
+                                      const float* tscale, int64_t rows, int64_t cols,
+                                      uint32_t rht_mask, bool bf16_out, void* out,
+                                      hipStream_t s) {
+  const int64_t nblk = rows * cols / 16;
+  if (nblk == 0) return hipSuccess;
+  int64_t grid = (nblk + kThreads - 1) / kThreads;
+  if (grid > 8192) grid = 8192;
+  if (bf16_out)
+    dequant_rht_kernel<true><<<grid, kThreads, 0, s>>>((const uint2*)data, scales, tscale, nblk,
+                                                       rht_mask, out);
+  else
+    dequant_rht_kernel<false><<<grid, kThreads, 0, s>>>((const uint2*)data, scales, tscale, nblk,
+                                                        rht_mask, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
                              int64_t rows, int64_t cols, bool bf16_out, void* out,

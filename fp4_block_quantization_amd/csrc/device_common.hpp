@@ -149,11 +149,9 @@ __device__ __forceinline__ float e2m1_sr_mag(float f, float q) {
   return __builtin_ldexpf(__builtin_ceilf(y - q), e - 2);
 }
 // ---- random-sign 16-point Hadamard transform ---------------------------------------
-// y_k = x_k * (+-1/4) (sign k from bit k of `mask`), then butterflies with strides
-// 1, 2, 4, 8: (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h).
-__device__ __forceinline__ void rht16(float (&y)[16], uint32_t mask) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) y[k] *= ((mask >> k) & 1u) ? -0.25f : 0.25f;
+// Butterflies with strides 1, 2, 4, 8: (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h); the
+// result is H16 y (Sylvester order).
+__device__ __forceinline__ void fwht16(float (&y)[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -164,6 +162,22 @@ __device__ __forceinline__ void rht16(float (&y)[16], uint32_t mask) {
       y[j + h] = a - b;
     }
   }
+}
+
+// Forward transform: y_k = x_k * (+-1/4) (sign k from bit k of `mask`), then H16.
+__device__ __forceinline__ void rht16(float (&y)[16], uint32_t mask) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) y[k] *= ((mask >> k) & 1u) ? -0.25f : 0.25f;
+  fwht16(y);
+}
+
+// Inverse transform ((H/4)^-1 = H/4, S^-1 = S): y_k *= 1/4, then H16, then the signs.
+__device__ __forceinline__ void irht16(float (&y)[16], uint32_t mask) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) y[k] *= 0.25f;
+  fwht16(y);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) y[k] = ((mask >> k) & 1u) ? -y[k] : y[k];
 }
 
 // ---- one candidate scale for one 16-value block ------------------------------------

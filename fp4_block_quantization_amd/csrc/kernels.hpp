@@ -41,6 +41,13 @@ hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const f
                              int64_t rows, int64_t cols, bool bf16_out, void* out,
                              hipStream_t stream);
 
+// Dequantize a record made with the random Hadamard transform (sign mask `rht_mask`)
+// and apply the inverse transform to every 16-value block.
+hipError_t launch_dequantize_hadamard(const uint8_t* data, const uint8_t* scales,
+                                      const float* tscale, int64_t rows, int64_t cols,
+                                      uint32_t rht_mask, bool bf16_out, void* out,
+                                      hipStream_t stream);
+
 hipError_t launch_qlinear(const uint8_t* xd, const uint8_t* xs, const float* xt,
                           const uint8_t* wd, const uint8_t* ws, const float* wt, int64_t M,
                           int64_t N, int64_t K, uint16_t* y, hipStream_t stream);

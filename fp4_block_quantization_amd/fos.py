@@ -155,6 +155,14 @@ def fos_dequantize(data: torch.Tensor, scales: torch.Tensor, tensor_scale: torch
                                _ptr(out), _stream(out.device)), "fos_dequantize")
 
 
+def fos_dequantize_hadamard(data: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Tensor,
+                            rows: int, cols: int, hadamard_seed: int, out: torch.Tensor) -> None:
+    dt = {torch.float32: FOS_OUT_F32, torch.bfloat16: FOS_OUT_BF16}[out.dtype]
+    _check(_lib.fos_dequantize_hadamard(_ptr(data), _ptr(scales), _ptr(tensor_scale), rows, cols,
+                                        hadamard_seed, dt, _ptr(out), _stream(out.device)),
+           "fos_dequantize_hadamard")
+
+
 def fos_qlinear_fwd(x_data, x_scales, x_t, w_data, w_scales, w_t, M: int, N: int, K: int,
                     y: torch.Tensor) -> None:
     _check(_lib.fos_qlinear_fwd(_ptr(x_data), _ptr(x_scales), _ptr(x_t), _ptr(w_data),
@@ -237,10 +245,18 @@ def quantize(x: torch.Tensor, rule: str = "4/6", rounding: str = "rne", block: s
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.float32,
+               inverse_hadamard: bool = False) -> torch.Tensor:
+    """Dequantize a record ([R, C] as stored).  With ``inverse_hadamard`` a record made
+    with the random Hadamard transform is returned to the original basis."""
     R, C = q.shape
     out = torch.empty(R, C, dtype=dtype, device=q.data.device)
-    fos_dequantize(q.data, q.scales, q.tensor_scale, R, C, out)
+    if inverse_hadamard:
+        if q.hadamard_seed is None:
+            raise ValueError("the record was not made with the Hadamard transform")
+        fos_dequantize_hadamard(q.data, q.scales, q.tensor_scale, R, C, q.hadamard_seed, out)
+    else:
+        fos_dequantize(q.data, q.scales, q.tensor_scale, R, C, out)
     return out
 
 

@@ -148,6 +148,21 @@ fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales,
                           const float* tensor_scale, int64_t rows, int64_t cols,
                           int out_dtype, void* out, void* stream);
 
+/* Dequantize a record made with the random Hadamard transform (cfg->hadamard with
+ * seed `hadamard_seed`) back to the original basis: fos_dequantize's fp32 values,
+ * then for every 16-value block of the record's rows the inverse transform, in fp32
+ * and in this order: multiply by 1/4, the 16-point Walsh-Hadamard butterflies
+ * (strides 1, 2, 4, 8), then the tensor's signs (the transform is orthogonal, so
+ * its inverse is its transpose).  FOS_OUT_BF16 rounds the result to nearest-even.
+ * The Four Over Six documentation page lists the transform among the quantization
+ * options; the Ultralytics glossary "FP4" (FP4 for inference and training) notes
+ * that such transforms spread outliers.  For a column-wise record the result is
+ * X^T.  Arguments, layout and errors as for fos_dequantize. */
+fos_status fos_dequantize_hadamard(const uint8_t* data, const uint8_t* scales,
+                                   const float* tensor_scale, int64_t rows, int64_t cols,
+                                   uint64_t hadamard_seed, int out_dtype, void* out,
+                                   void* stream);
+
 /* Simulated quantized linear forward (Four Over Six documentation page, "Four Over
  * Six": without native FP4 matmuls the layer is simulated with a higher-precision
  * matrix multiplication of the dequantized operands):

@@ -10,7 +10,10 @@ construction; readings taken here:
     Philox4x32-10(key = seed, counter = (0, 0, 0, 0)), set bit -> -1;
   * in fp32, each value is first multiplied by s_k/4 (exact for bf16 inputs), then
     the in-place fast Walsh-Hadamard butterflies run with strides 1, 2, 4, 8:
-    (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h) for every j with (j & h) == 0.
+    (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h) for every j with (j & h) == 0;
+  * the inverse (for dequantizing back to the original basis) uses that (H/4)^-1 =
+    H/4 and S^-1 = S: multiply by 1/4, run the same butterflies, then apply the signs
+    (all in fp32, in that order).
 """
 from __future__ import annotations
 
@@ -42,3 +45,9 @@ def rht_blocks(blocks: np.ndarray, signs: np.ndarray) -> np.ndarray:
             out[..., j + h] = a - b
         y = out
     return y.astype(np.float32)
+
+
+def irht_blocks(blocks: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Inverse transform of each row of ``blocks`` (n, 16), float32 -> float32."""
+    return (rht_blocks(blocks, np.ones(16, dtype=np.float32)) * signs.astype(np.float32)
+            ).astype(np.float32)

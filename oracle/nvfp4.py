@@ -64,7 +64,7 @@ import numpy as np
 from .formats import (E2M1_GRID, bf16_bits_to_f32, e2m1_rne_code, e4m3_rne_sat,
                       e4m3_value)
 from .fparith import fma32
-from .hadamard import rht_blocks, rht_signs
+from .hadamard import irht_blocks, rht_blocks, rht_signs
 from .philox import philox4x32_10, split_seed
 
 F32 = np.float32
@@ -315,3 +315,13 @@ def dequantize(data: np.ndarray, scales: np.ndarray, t) -> np.ndarray:
     val = (mag * d[..., None].astype(np.float64)).astype(F32)      # one rounding
     val = np.where((q & 8) != 0, -val, val).astype(F32)
     return val.reshape(R, C)
+
+
+def dequantize_hadamard(data: np.ndarray, scales: np.ndarray, t, seed: int) -> np.ndarray:
+    """Dequantize a record made with the random Hadamard transform (seed ``seed``) and
+    return it to the original basis: O8, then the inverse transform of every
+    16-value block of the record's rows (fp32)."""
+    val = dequantize(data, scales, t)
+    R, C = val.shape
+    back = irht_blocks(val.reshape(-1, 16), rht_signs(seed))
+    return back.reshape(R, C).astype(F32)

@@ -93,6 +93,16 @@ def test_dequantize_validation():
     assert L.fos_dequantize(None, None, None, 0, 32, 0, None, None) == fos.FOS_OK   # empty
 
 
+def test_dequantize_hadamard_validation():
+    L = fos.lib()
+    f = FAKE
+    assert L.fos_dequantize_hadamard(f, f, f, 4, 40, 1, 0, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_dequantize_hadamard(f, f, f, 4, 32, 1, 7, f, None) == fos.FOS_E_FLAGS
+    assert L.fos_dequantize_hadamard(None, f, f, 4, 32, 1, 0, f, None) == fos.FOS_E_NULL
+    assert L.fos_dequantize_hadamard(f, f, f, 4, 32, 1, 0, MIS, None) == fos.FOS_E_ALIGN
+    assert L.fos_dequantize_hadamard(None, None, None, 0, 32, 1, 0, None, None) == fos.FOS_OK
+
+
 def test_qlinear_validation():
     L = fos.lib()
     f = FAKE

@@ -431,3 +431,56 @@ def test_qlinear_bwd_end_to_end_with_hadamard(fos):
     exact = F.bf16_bits_to_f32(gb).astype(np.float64).T @ F.bf16_bits_to_f32(xb).astype(np.float64)
     got = F.bf16_bits_to_f32(bits_of(dw.cpu())).astype(np.float64)
     assert np.linalg.norm(got - exact) / np.linalg.norm(exact) < 0.15
+
+
+# ------------------------------------------------------------------ inverse Hadamard
+
+@pytest.mark.parametrize("cfg_name", ["row_rht", "row_rht_sr", "col_rht", "col_rht_sr"])
+@pytest.mark.parametrize("shape", [(48, 80), (272, 1040)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_dequantize_hadamard_matches_oracle(fos, cfg_name, shape):
+    """Records from the oracle, dequantized and inverse-transformed on the GPU:
+    fp32 and bf16 outputs bit-exact."""
+    cfg = CFGS[cfg_name]
+    bits = bits_of(W.random_bf16(*shape, seed=53, dist="student_t"))
+    o = N.quantize(bits, cfg)
+    lay = "row" if cfg.rows_out else "col"
+    q = _dev_record(fos, o, lay)
+    q.hadamard_seed = cfg.hadamard_seed
+    want = N.dequantize_hadamard(o[f"{lay}_data"], o[f"{lay}_scales"], o["t"], cfg.hadamard_seed)
+    got32 = fos.dequantize(q, torch.float32, inverse_hadamard=True).cpu().numpy()
+    assert np.array_equal(got32.view(np.uint32), want.view(np.uint32))
+    got16 = bits_of(fos.dequantize(q, torch.bfloat16, inverse_hadamard=True).cpu())
+    assert_same_bytes(got16, F.f32_to_bf16_bits(want), "bf16")
+
+
+def test_hadamard_round_trip_on_gpu(fos):
+    """GPU quantize with the transform, GPU dequantize with the inverse: the original
+    tensor within the format's error (and the same bytes as the oracle's path)."""
+    bits = bits_of(W.random_bf16(512, 1024, 61, "normal"))
+    x = to_gpu_bf16(bits)
+    q = fos.quantize(x, hadamard_seed=13)
+    back = fos.dequantize(q, torch.float32, inverse_hadamard=True).cpu().numpy().astype(np.float64)
+    xf = F.bf16_bits_to_f32(bits).astype(np.float64)
+    assert np.linalg.norm(back - xf) / np.linalg.norm(xf) < 0.15
+    o = N.quantize(bits, N.Config(hadamard=True, hadamard_seed=13))
+    want = N.dequantize_hadamard(o["row_data"], o["row_scales"], o["t"], 13)
+    assert np.array_equal(back.astype(np.float32).view(np.uint32), want.view(np.uint32))
+
+
+def test_qlinear_with_hadamard_on_both_operands(fos):
+    """X and W quantized row-wise with the same transform seed: the transform cancels
+    in the product, Y matches the oracle's reference from those records and
+    approximates X W^T."""
+    m, n, k = 256, 512, 1024
+    xb = bits_of(W.random_bf16(m, k, 71, "student_t"))
+    wb = bits_of(W.random_bf16(n, k, 73, "normal", scale=0.02))
+    xq = fos.quantize(to_gpu_bf16(xb), hadamard_seed=17)
+    wq = fos.quantize(to_gpu_bf16(wb), hadamard_seed=17)
+    y = bits_of(fos.qlinear_fwd(xq, wq).cpu())
+    cfg = N.Config(hadamard=True, hadamard_seed=17)
+    ox, ow = N.quantize(xb, cfg), N.quantize(wb, cfg)
+    _qlinear_check(y, ox["row_data"], ox["row_scales"], ox["t"], ow["row_data"], ow["row_scales"],
+                   ow["t"])
+    exact = F.bf16_bits_to_f32(xb).astype(np.float64) @ F.bf16_bits_to_f32(wb).astype(np.float64).T
+    got = F.bf16_bits_to_f32(y).astype(np.float64)
+    assert np.linalg.norm(got - exact) / np.linalg.norm(exact) < 0.15

@@ -110,3 +110,51 @@ def test_rht_signs_from_philox_word0():
     assert w0 == 0x6627E8D5
     s = rht_signs(0)
     assert [int(v < 0) for v in s] == [(w0 >> k) & 1 for k in range(16)]
+
+
+# ------------------------------------------------------------------ inverse transform
+
+def test_inverse_hadamard_exact_round_trip_on_small_integers():
+    """Small integer blocks: every fp32 operation of both transforms is exact (sums of
+    at most 16 quarter-integers), so the round trip returns the input bit for bit."""
+    from oracle.hadamard import irht_blocks
+    rng = np.random.default_rng(3)
+    x = rng.integers(-8, 9, size=(64, 16)).astype(np.float32)
+    for seed in (0, 1, 99, 2 ** 40 + 7):
+        s = rht_signs(seed)
+        back = irht_blocks(rht_blocks(x, s), s)
+        assert np.array_equal(back, x)
+
+
+def test_inverse_hadamard_matches_scipy():
+    """irht(y) = S (H/4) y in fp64, within fp32 rounding of the butterflies."""
+    from oracle.hadamard import irht_blocks
+    H = scipy.linalg.hadamard(16).astype(np.float64)
+    rng = np.random.default_rng(4)
+    y = rng.standard_normal((32, 16)).astype(np.float32)
+    for seed in (5, 6):
+        s = rht_signs(seed).astype(np.float64)
+        want = (y.astype(np.float64) @ (H / 4.0).T) * s
+        got = irht_blocks(y, rht_signs(seed)).astype(np.float64)
+        assert np.max(np.abs(got - want)) <= 8 * 2.0 ** -24 * np.max(np.abs(y)) * 4
+
+
+def test_dequantize_hadamard_returns_to_the_original_basis():
+    """quantize with the transform, dequantize with the inverse: back to x within the
+    format's error; the wrong seed gives garbage."""
+    from oracle import formats as F
+    from oracle import nvfp4 as N
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    xb = F.f32_to_bf16_bits(x)
+    xf = F.bf16_bits_to_f32(xb).astype(np.float64)
+    for cfg in (N.Config(hadamard=True, hadamard_seed=21),
+                N.Config(rows_out=False, cols_out=True, hadamard=True, hadamard_seed=21)):
+        q = N.quantize(xb, cfg)
+        lay = "row" if cfg.rows_out else "col"
+        ref = xf if lay == "row" else xf.T
+        good = N.dequantize_hadamard(q[f"{lay}_data"], q[f"{lay}_scales"], q["t"], 21)
+        bad = N.dequantize_hadamard(q[f"{lay}_data"], q[f"{lay}_scales"], q["t"], 22)
+        rel = lambda v: np.linalg.norm(v.astype(np.float64) - ref) / np.linalg.norm(ref)
+        assert rel(good) < 0.15
+        assert rel(bad) > 0.5
