@@ -7,7 +7,8 @@
 // values), so every store instruction of a wave covers 1 KB of contiguous memory; it
 // reads the 2 or 4 nibble bytes of its chunk (contiguous across lanes) and the block's
 // scale byte (shared by the 4 or 2 lanes of a block).  Hardware E2M1 -> fp32
-// conversion; bf16 output rounds the fp32 value to nearest-even.
+// conversion; bf16 output rounds the fp32 value to nearest-even.  The inverse-Hadamard
+// variant needs whole blocks per lane (32 or 64 bytes out per lane).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -58,6 +59,40 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   for (; g < nchunk; g += stride) dequant_chunk<kBF16>(data, scales, t, g, out);
 }
 
+// Dequantize one 16-value block (8 nibble bytes + its scale byte) into v.
+__device__ __forceinline__ void dequant_block(uint2 q, uint32_t s, float t, float (&v)[16]) {
+  const float d = e4m3_decode(s) * t;
+  const f32x2 e[8] = {cvt_pk_f32_fp4<0>(q.x), cvt_pk_f32_fp4<1>(q.x), cvt_pk_f32_fp4<2>(q.x),
+                      cvt_pk_f32_fp4<3>(q.x), cvt_pk_f32_fp4<0>(q.y), cvt_pk_f32_fp4<1>(q.y),
+                      cvt_pk_f32_fp4<2>(q.y), cvt_pk_f32_fp4<3>(q.y)};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[2 * j] = e[j].x * d;
+    v[2 * j + 1] = e[j].y * d;
+  }
+}
+
+// Store block b's 16 values: 32 bytes of bf16 (RNE) or 64 bytes of fp32.
+template <bool kBF16>
+__device__ __forceinline__ void store_values(void* out, int64_t b, const float (&v)[16]) {
+  if (kBF16) {
+    uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 w;
+      w.x = f32_to_bf16_rne(v[8 * h + 0]) | (f32_to_bf16_rne(v[8 * h + 1]) << 16);
+      w.y = f32_to_bf16_rne(v[8 * h + 2]) | (f32_to_bf16_rne(v[8 * h + 3]) << 16);
+      w.z = f32_to_bf16_rne(v[8 * h + 4]) | (f32_to_bf16_rne(v[8 * h + 5]) << 16);
+      w.w = f32_to_bf16_rne(v[8 * h + 6]) | (f32_to_bf16_rne(v[8 * h + 7]) << 16);
+      o[h] = w;
+    }
+  } else {
+    float4* o = reinterpret_cast<float4*>(out) + 4 * b;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) o[h] = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+  }
+}
+
 // Records made with the random Hadamard transform, returned to the original basis:
 // lane = one 16-value block (8 nibble bytes + 1 scale byte in, 32 or 64 bytes out);
 // values are dequantized exactly as above, then inverse-transformed in registers.
@@ -70,35 +105,10 @@ __global__ __launch_bounds__(kThreads) void dequant_rht_kernel(const uint2* __re
   const float t = tscale[0];
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    const uint2 q = data[b];
-    const float d = e4m3_decode(scales[b]) * t;
-    const f32x2 e[8] = {cvt_pk_f32_fp4<0>(q.x), cvt_pk_f32_fp4<1>(q.x), cvt_pk_f32_fp4<2>(q.x),
-                        cvt_pk_f32_fp4<3>(q.x), cvt_pk_f32_fp4<0>(q.y), cvt_pk_f32_fp4<1>(q.y),
-                        cvt_pk_f32_fp4<2>(q.y), cvt_pk_f32_fp4<3>(q.y)};
     float v[16];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[2 * j] = e[j].x * d;
-      v[2 * j + 1] = e[j].y * d;
-    }
+    dequant_block(data[b], scales[b], t, v);
     irht16(v, mask);
-    if (kBF16) {
-      uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint4 w;
-        w.x = f32_to_bf16_rne(v[8 * h + 0]) | (f32_to_bf16_rne(v[8 * h + 1]) << 16);
-        w.y = f32_to_bf16_rne(v[8 * h + 2]) | (f32_to_bf16_rne(v[8 * h + 3]) << 16);
-        w.z = f32_to_bf16_rne(v[8 * h + 4]) | (f32_to_bf16_rne(v[8 * h + 5]) << 16);
-        w.w = f32_to_bf16_rne(v[8 * h + 6]) | (f32_to_bf16_rne(v[8 * h + 7]) << 16);
-        o[h] = w;
-      }
-    } else {
-      float4* o = reinterpret_cast<float4*>(out) + 4 * b;
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        o[h] = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
-    }
+    store_values<kBF16>(out, b, v);
   }
 }
 

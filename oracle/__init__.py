@@ -25,4 +25,4 @@ of readings is kept with the design notes.  Functions whose result the pages and
 mathematics pin are tested against those pins in ``tests/test_oracle_*.py``.
 """
 
-from . import formats, fparith, philox, hadamard, nvfp4, qlinear, page_example  # noqa: F401
+from . import formats, fparith, philox, hadamard, nvfp4, qlinear, mxfp4, page_example  # noqa: F401
