@@ -298,4 +298,52 @@ fos_status fos_qlinear_bwd(const uint8_t* dy_data, const uint8_t* dy_scales,
   return FOS_OK;
 }
 
+fos_status fos_mx_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* data,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
+  if (cols % 32) return FOS_E_SHAPE;
+  if (rows * cols == 0) return FOS_OK;
+  if (!x || !data || !scales) return FOS_E_NULL;
+  if (!aligned(x, 16) || !aligned(data, 16)) return FOS_E_ALIGN;
+  return fos::launch_mx_quantize(static_cast<const uint16_t*>(x), rows, cols, data, scales,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
+fos_status fos_mx_dequantize(const uint8_t* data, const uint8_t* scales, int64_t rows,
+                             int64_t cols, int out_dtype, void* out, void* stream) {
+  if (out_dtype != FOS_OUT_F32 && out_dtype != FOS_OUT_BF16) return FOS_E_FLAGS;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
+  if (cols % 32) return FOS_E_SHAPE;
+  if (rows * cols == 0) return FOS_OK;
+  if (!data || !scales || !out) return FOS_E_NULL;
+  if (!aligned(data, 4) || !aligned(out, 16)) return FOS_E_ALIGN;
+  return fos::launch_mx_dequantize(data, scales, rows, cols, out_dtype == FOS_OUT_BF16, out,
+                                   static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
+fos_status fos_mx_qlinear_fwd(const uint8_t* a_data, const uint8_t* a_scales,
+                              const uint8_t* b_data, const uint8_t* b_scales, int64_t M,
+                              int64_t N, int64_t K, void* y_bf16, void* stream) {
+  if (M < 1 || N < 1 || K < 256 || K % 256 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return FOS_E_SHAPE;
+  if (N > kMaxElems / M || K > kMaxElems / M || K > kMaxElems / N) return FOS_E_SHAPE;
+  if ((M + 256) * (K / 2) >= ((int64_t)1 << 32) || (N + 256) * (K / 2) >= ((int64_t)1 << 32))
+    return FOS_E_SHAPE;
+  if (!a_data || !a_scales || !b_data || !b_scales || !y_bf16) return FOS_E_NULL;
+  if (!aligned(a_data, 16) || !aligned(b_data, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(y_bf16, 2))
+    return FOS_E_ALIGN;
+  return fos::launch_mx_gemm(a_data, a_scales, b_data, b_scales, M, N, K,
+                             static_cast<uint16_t*>(y_bf16), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
 }  // extern "C"

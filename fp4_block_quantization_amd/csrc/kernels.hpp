@@ -48,6 +48,16 @@ hipError_t launch_dequantize_hadamard(const uint8_t* data, const uint8_t* scales
                                       uint32_t rht_mask, bool bf16_out, void* out,
                                       hipStream_t stream);
 
+// MXFP4 (32 E2M1 values per E8M0 scale): quantize bf16 [rows][cols] (cols % 32 == 0),
+// dequantize, and the native FP4 GEMM Y = deq(A) deq(B)^T (K % 256 == 0).
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* data,
+                              uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx_dequantize(const uint8_t* data, const uint8_t* scales, int64_t rows,
+                                int64_t cols, bool bf16_out, void* out, hipStream_t stream);
+hipError_t launch_mx_gemm(const uint8_t* ad, const uint8_t* as, const uint8_t* bd,
+                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                          hipStream_t stream);
+
 hipError_t launch_qlinear(const uint8_t* xd, const uint8_t* xs, const float* xt,
                           const uint8_t* wd, const uint8_t* ws, const float* wt, int64_t M,
                           int64_t N, int64_t K, uint16_t* y, hipStream_t stream);

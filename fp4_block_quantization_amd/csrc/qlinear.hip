@@ -25,18 +25,19 @@
 // Workgroups are remapped so that each XCD (dispatched round-robin) runs a contiguous
 // group of 4 tile-rows x all tile-columns.
 #include "device_common.hpp"
+#include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace fos {
 
 namespace {
 
+using namespace gemm;
+
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 64;
-constexpr int kGroupM = 4;
 
 __device__ __forceinline__ h8 dequant8(uint32_t w, h2 dd) {
   const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * dd;
@@ -69,8 +70,6 @@ struct Operands {
   __amdgpu_buffer_rsrc_t a, sa, b, sb;
   uint32_t oa[TI], osa[TI], ob[TJ], osb[TJ];
 };
-
-constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -139,15 +138,8 @@ void qlinear_kernel(const uint8_t* __restrict__ xd, const uint8_t* __restrict__ 
   constexpr int kWM = 32 * TI, kWN = 32 * TJ;     // wave tile
   constexpr int kBM = 2 * kWM, kBN = 2 * kWN;     // workgroup tile
   // ---- tile assignment: contiguous range per XCD, grouped along M inside it
-  const int nwg = tiles_m * tiles_n;
-  const int w = blockIdx.x;
-  const int L = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (L / per_group) * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - first_m);
-  const int in_g = L % per_group;
-  const int tm = first_m + in_g % gsize;
-  const int tn = in_g / gsize;
+  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
+  const int tm = tc.tm, tn = tc.tn;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
@@ -260,13 +252,6 @@ struct LdsStage {
   uint8_t sa[kScaleBytes];
   uint8_t sb[kScaleBytes];
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base, uint32_t voff,
-                                      int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
-}
 
 struct LdsOperands {
   __amdgpu_buffer_rsrc_t a, sa, b, sb;
@@ -388,41 +373,6 @@ __device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4
   }
 }
 
-// Epilogue of a full 256x256 tile (Y below 4 GiB): scale by t_x * t_w, round pairs
-// to bf16 with the hardware conversion (nearest-even), and store 4 bytes per lane.
-// In the MFMA layout, element a of lane (lr, h) is row (a & 3) + 8 (a >> 2) + 4h,
-// column lr: elements a, a + 1 are vertically adjacent, lanes lr, lr + 1 horizontally
-// adjacent.  Adjacent lanes swap one packed pair (DPP) so that the even lane holds
-// row r, columns (c, c + 1) and the odd lane row r + 1, columns (c - 1, c).  The row
-// offsets are scalar, so each store is one buffer instruction with no address math.
-__device__ __forceinline__ void store_tile_full(uint16_t* y, int M, int N, int m0, int n0,
-                                                int lr, int h, float s,
-                                                const f32x16 (&acc)[4][4]) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)y, 0, (int)((uint32_t)M * (uint32_t)N * 2u), kRsrcWord3);
-  const int odd = lr & 1;
-  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-  const uint32_t row_bytes = (uint32_t)N * 2u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const uint32_t voff = (uint32_t)(m0 + 32 * i + 4 * h + odd) * row_bytes +
-                            (uint32_t)(n0 + 32 * n + lr - odd) * 2u;
-#pragma unroll
-      for (int a = 0; a < 16; a += 2) {
-        const f32x2 v = {acc[i][n][a] * s, acc[i][n][a + 1] * s};
-        const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-        const uint32_t q = __builtin_amdgcn_update_dpp(0u, p, 0xB1, 0xF, 0xF, false);
-        const uint32_t out = __builtin_amdgcn_perm(q, p, sel);
-        const int drow = (a & 3) + 8 * (a >> 2);
-        __builtin_amdgcn_raw_buffer_store_b32(out, ry, voff, (int)(drow * row_bytes), 0);
-      }
-    }
-  }
-}
-
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void qlinear_lds_kernel(const uint8_t* __restrict__ xd, const uint8_t* __restrict__ xs,
                         const float* __restrict__ xt, const uint8_t* __restrict__ wd,
@@ -431,15 +381,8 @@ void qlinear_lds_kernel(const uint8_t* __restrict__ xd, const uint8_t* __restric
   __shared__ __attribute__((aligned(16))) LdsStage st0;
   __shared__ __attribute__((aligned(16))) LdsStage st1;
   // ---- tile assignment: contiguous range per XCD, grouped along M inside it
-  const int nwg = tiles_m * tiles_n;
-  const int w = blockIdx.x;
-  const int L = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (L / per_group) * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - first_m);
-  const int in_g = L % per_group;
-  const int tm = first_m + in_g % gsize;
-  const int tn = in_g / gsize;
+  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
+  const int tm = tc.tm, tn = tc.tn;
 
   // the wave index is made explicitly uniform so that the LDS destinations of the
   // direct loads (M0) are scalar values rather than per-lane registers
@@ -501,27 +444,7 @@ void qlinear_lds_kernel(const uint8_t* __restrict__ xd, const uint8_t* __restric
     stage_mma(st0, acc, ra, rb, h);
   }
 
-  const int m0 = tm * kTileRows + (wave >> 1) * 128;
-  const int n0 = tn * kTileRows + (wave & 1) * 128;
-  const float s = xt[0] * wt[0];
-  if ((tm + 1) * kTileRows <= M && (tn + 1) * kTileRows <= N &&
-      (int64_t)M * N * 2 < ((int64_t)1 << 32)) {
-    store_tile_full(y, M, N, m0, n0, lr, h, s, acc);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int col = n0 + 32 * n + lr;
-        if (col >= N) continue;
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int row = m0 + 32 * i + (a & 3) + 8 * (a >> 2) + 4 * h;
-          if (row < M) y[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][n][a] * s);
-        }
-      }
-    }
-  }
+  store_tile(y, M, N, tm, tn, wave, lr, h, xt[0] * wt[0], acc);
 }
 
 hipError_t launch_lds(const uint8_t* xd, const uint8_t* xs, const float* xt, const uint8_t* wd,

@@ -57,6 +57,9 @@ def _load() -> ctypes.CDLL:
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_qlinear_fwd": ([P, P, P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
         "fos_qlinear_bwd": ([P] * 12 + [I64, I64, I64, P, P, P], ctypes.c_int),
+        "fos_mx_quantize": ([P, I64, I64, P, P, P], ctypes.c_int),
+        "fos_mx_dequantize": ([P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
+        "fos_mx_qlinear_fwd": ([P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -311,3 +314,52 @@ def qlinear_bwd(dyq: Optional[NVFP4Tensor], dyq_t: Optional[NVFP4Tensor],
                     trip(xq_t) if need_dw else None, trip(wq_t) if need_dx else None,
                     M, N, K, dx, dw)
     return dx, dw
+
+
+# ---------------------------------------------------------------- MXFP4
+
+@dataclass
+class MXFP4Tensor:
+    """One MXFP4 record: data [R, C/2] nibbles and scales [R, C/32] E8M0 bytes."""
+    data: torch.Tensor
+    scales: torch.Tensor
+
+    @property
+    def shape(self) -> Tuple[int, int]:
+        return (self.data.shape[0], self.data.shape[1] * 2)
+
+
+def mx_quantize(x: torch.Tensor) -> MXFP4Tensor:
+    """MXFP4 quantization of a bf16 [R, C] tensor (C % 32 == 0)."""
+    _check_input(x)
+    R, C = x.shape
+    u8 = dict(dtype=torch.uint8, device=x.device)
+    data, scales = torch.empty(R, C // 2, **u8), torch.empty(R, C // 32, **u8)
+    _check(_lib.fos_mx_quantize(_ptr(x), R, C, _ptr(data), _ptr(scales), _stream(x.device)),
+           "fos_mx_quantize")
+    return MXFP4Tensor(data, scales)
+
+
+def mx_dequantize(q: MXFP4Tensor, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    R, C = q.shape
+    out = torch.empty(R, C, dtype=dtype, device=q.data.device)
+    dt = {torch.float32: FOS_OUT_F32, torch.bfloat16: FOS_OUT_BF16}[dtype]
+    _check(_lib.fos_mx_dequantize(_ptr(q.data), _ptr(q.scales), R, C, dt, _ptr(out),
+                                  _stream(out.device)), "fos_mx_dequantize")
+    return out
+
+
+def mx_qlinear_fwd(aq: MXFP4Tensor, bq: MXFP4Tensor, out: Optional[torch.Tensor] = None
+                   ) -> torch.Tensor:
+    """Y = deq(A) deq(B)^T in bf16 on the FP4 matrix cores; A [M, K], B [N, K]."""
+    M, K = aq.shape
+    N, K2 = bq.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=aq.data.device)
+    if y.shape != (M, N) or y.dtype != torch.bfloat16 or not y.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    _check(_lib.fos_mx_qlinear_fwd(_ptr(aq.data), _ptr(aq.scales), _ptr(bq.data), _ptr(bq.scales),
+                                   M, N, K, _ptr(y), _stream(y.device)), "fos_mx_qlinear_fwd")
+    return y
+

@@ -210,6 +210,39 @@ fos_status fos_qlinear_bwd(const uint8_t* dy_data, const uint8_t* dy_scales,
                            int64_t M, int64_t N, int64_t K, void* dx_bf16, void* dw_bf16,
                            void* stream);
 
+/* ---- MXFP4 -------------------------------------------------------------------
+ * Ultralytics glossary "FP4", "How FP4 works": MXFP4 (OCP Microscaling) groups 32
+ * E2M1 values under one power-of-two E8M0 scale; "FP4 for inference and training":
+ * MI350-class accelerators multiply it natively.  No per-tensor scale.
+ * Record layout: data [R][C/2] nibbles as for NVFP4; scales [R][C/32] E8M0 bytes
+ * (value 2^(byte - 127)).
+ * Scale rule (the OCP MX specification's; the page names the specification but not
+ * the rule): e = floor(log2(max |x| of the block)) - 2, clamped to [-127, 127], -127
+ * for a block of zeros; elements are E2M1 round-to-nearest-even of x / 2^e,
+ * saturating at 6, zeros keeping the sign of x. */
+
+/* MXFP4 quantization of bf16 x [rows][cols] (16-byte aligned), cols % 32 == 0;
+ * data 16-byte aligned.  Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_mx_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* data,
+                           uint8_t* scales, void* stream);
+
+/* out[r][c] = E2M1(q) * 2^(scale - 127) (exact in fp32; FOS_OUT_BF16 rounds it to
+ * nearest-even).  data 4-byte aligned, out 16-byte aligned, cols % 32 == 0.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_HIP. */
+fos_status fos_mx_dequantize(const uint8_t* data, const uint8_t* scales, int64_t rows,
+                             int64_t cols, int out_dtype, void* out, void* stream);
+
+/* Native FP4 linear: Y[m][n] = bf16( sum_k deq(A)[m][k] * deq(B)[n][k] ) for MXFP4
+ * records A [M][K] and B [N][K] blocked along K, on the scaled FP4 matrix cores
+ * (E2M1 x E2M1 products with the two E8M0 block scales, fp32 accumulation).
+ *   M, N >= 1; K >= 256 and K % 256 == 0; (M + 256) * K / 2 and (N + 256) * K / 2
+ *   below 2^32.  a_data, b_data 16-byte aligned; a_scales, b_scales 4-byte
+ *   aligned; y_bf16 [M][N] 2-byte aligned.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_mx_qlinear_fwd(const uint8_t* a_data, const uint8_t* a_scales,
+                              const uint8_t* b_data, const uint8_t* b_scales, int64_t M,
+                              int64_t N, int64_t K, void* y_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

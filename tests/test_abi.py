@@ -103,6 +103,23 @@ def test_dequantize_hadamard_validation():
     assert L.fos_dequantize_hadamard(None, None, None, 0, 32, 1, 0, None, None) == fos.FOS_OK
 
 
+def test_mx_validation():
+    L = fos.lib()
+    f = FAKE
+    assert L.fos_mx_quantize(f, 4, 48, f, f, None) == fos.FOS_E_SHAPE          # cols % 32
+    assert L.fos_mx_quantize(None, 4, 64, f, f, None) == fos.FOS_E_NULL
+    assert L.fos_mx_quantize(MIS, 4, 64, f, f, None) == fos.FOS_E_ALIGN
+    assert L.fos_mx_quantize(f, 4, 64, ctypes.c_void_p(0x100008), f, None) == fos.FOS_E_ALIGN
+    assert L.fos_mx_quantize(None, 0, 64, None, None, None) == fos.FOS_OK
+    assert L.fos_mx_dequantize(f, f, 4, 48, 0, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_mx_dequantize(f, f, 4, 64, 9, f, None) == fos.FOS_E_FLAGS
+    assert L.fos_mx_dequantize(f, f, 4, 64, 0, MIS, None) == fos.FOS_E_ALIGN
+    assert L.fos_mx_qlinear_fwd(f, f, f, f, 256, 256, 128, f, None) == fos.FOS_E_SHAPE   # K % 256
+    assert L.fos_mx_qlinear_fwd(f, f, f, f, 0, 256, 256, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_mx_qlinear_fwd(None, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_NULL
+    assert L.fos_mx_qlinear_fwd(MIS, f, f, f, 256, 256, 256, f, None) == fos.FOS_E_ALIGN
+
+
 def test_qlinear_validation():
     L = fos.lib()
     f = FAKE
