@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, published (2.5 PFLOP/s)
+FP4_MFMA_PEAK_TFLOPS = 10066.3  # MI355X dense fp4 MFMA, published (10.1 PFLOP/s)
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp4_block_quantization_amd", "csrc", f)
                   for f in ("quantize.hip", "device_common.hpp")]
@@ -244,6 +245,46 @@ def bench_qlinear_bwd(fos, x_cpu, w_cpu, dy_cpu, steps, warmup):
             "TFLOPs": flops / ms / 1e9, "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
 
 
+def bench_mx(fos, x_cpu, w_cpu, x2_cpu, steps, warmup):
+    """MXFP4: quantize the c2 weight (GB/s) and the c5 layer on the FP4 matrix cores."""
+    import ctypes
+    import torch
+    dev = "cuda:0"
+    lib = fos.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    R, C = x2_cpu.shape
+    sets = 3
+    xs = [x2_cpu.to(dev) for _ in range(sets)]
+    u8 = dict(dtype=torch.uint8, device=dev)
+    outs = [(torch.empty(R, C // 2, **u8), torch.empty(R, C // 32, **u8)) for _ in range(sets)]
+    args = [(_vp(xs[i]), R, C, _vp(outs[i][0]), _vp(outs[i][1]), stream) for i in range(sets)]
+    f = lib.fos_mx_quantize
+    bad = [0]
+
+    def fq(i):
+        bad[0] |= f(*args[i])
+    ms_q = time_loop(fq, steps, warmup, sets)
+    qb = 2 * R * C + R * C // 2 + R * C // 32
+    aq = fos.mx_quantize(x_cpu.to(dev))
+    bq = fos.mx_quantize(w_cpu.to(dev))
+    M, K = aq.shape
+    N = bq.shape[0]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    g = lib.fos_mx_qlinear_fwd
+    gargs = (_vp(aq.data), _vp(aq.scales), _vp(bq.data), _vp(bq.scales), M, N, K, _vp(y), stream)
+
+    def fg(i):
+        bad[0] |= g(*gargs)
+    ms_g = time_loop(fg, max(10, steps // 2), max(30, warmup), 1)
+    if bad[0]:
+        raise RuntimeError("an MXFP4 call returned an error status")
+    flops = 2 * M * N * K
+    return {"quantize_c2": {"bytes": qb, "ms": ms_q, "GBps": qb / ms_q / 1e6,
+                            "frac": qb / ms_q / 1e6 / HBM_PEAK_GBS},
+            "gemm_c5": {"shape": [M, N, K], "flop": flops, "ms": ms_g, "TFLOPs": flops / ms_g / 1e9,
+                        "frac_fp4_peak": flops / ms_g / 1e9 / FP4_MFMA_PEAK_TFLOPS}}
+
+
 def copy_reference(steps):
     """A plain device-to-device copy (torch's copy kernel) of 256 MiB: a measured
     ceiling for streaming read+write traffic on this GPU."""
@@ -371,6 +412,10 @@ def main():
     rows["c5_qlinear_bwd"] = bench_qlinear_bwd(fos, W.make("c5_x"), W.make("c5_w"),
                                                W.make("c5_dy"), args.steps, args.warmup)
     log(json.dumps(rows["c5_qlinear_bwd"]))
+
+    log("MXFP4 ...")
+    rows["mxfp4"] = bench_mx(fos, W.make("c5_x"), W.make("c5_w"), x2, args.steps, args.warmup)
+    log(json.dumps(rows["mxfp4"]))
 
     cpu = None
     if not args.no_cpu:
