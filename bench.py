@@ -331,7 +331,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one piece (c2_step, c2_kernel, c3_kernel, c4a_kernel, "
-                         "c4b_kernel, c5_qlinear, copy) and exit")
+                         "c4b_kernel, c5_qlinear, c5_mx_gemm, copy) and exit")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -355,6 +355,15 @@ def main():
                 fos.qlinear_fwd(xq, wq, out=y)
             torch.cuda.synchronize()
             log(f"ran c5_qlinear x{args.steps}")
+            return
+        if args.only == "c5_mx_gemm":
+            aq = fos.mx_quantize(W.make("c5_x").to("cuda:0"))
+            bq = fos.mx_quantize(W.make("c5_w").to("cuda:0"))
+            y = fos.mx_qlinear_fwd(aq, bq)
+            for _ in range(args.steps):
+                fos.mx_qlinear_fwd(aq, bq, out=y)
+            torch.cuda.synchronize()
+            log(f"ran c5_mx_gemm x{args.steps}")
             return
         if args.only == "copy":
             a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda:0")

@@ -192,6 +192,8 @@ __device__ __forceinline__ i32x8 mx_operand(const uint8_t* base, int row, int g)
 constexpr int NKS = kMxSuper / 64;
 __device__ __forceinline__ void mx_stage_mma(const MxStage& st, f32x16 (&acc)[4][4], int ra,
                                              int rb, int h) {
+  // keep the caller's copies of the next stage ahead of this stage's MFMAs
+  __builtin_amdgcn_sched_barrier(0);
   uint2 sa[4], sb[4];
   i32x8 A[4], B[4];
 #pragma unroll
@@ -232,6 +234,9 @@ __device__ __forceinline__ void mx_stage_mma(const MxStage& st, f32x16 (&acc)[4]
       }
     }
   }
+  // MFMAs touch no memory, so without this the scheduler may sink them below the
+  // next workgroup barrier, leaving the next stage's copies nothing to hide behind
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -290,14 +295,14 @@ void mx_gemm_kernel(const uint8_t* __restrict__ ad, const uint8_t* __restrict__ 
     mx_stage_mma(st0, acc, ra, rb, h);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (sc + 2 < nsc) mx_stage_load(st0, p, sc + 2, wave);
+    // unconditional (a redundant copy of the last stage when none is left): a branch
+    // here lets the compiler sink the previous stage's MFMAs past the barrier
+    mx_stage_load(st0, p, min(sc + 2, nsc - 1), wave);
     mx_stage_mma(st1, acc, ra, rb, h);
   }
-  if (sc < nsc) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    mx_stage_mma(st0, acc, ra, rb, h);
-  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (sc < nsc) mx_stage_mma(st0, acc, ra, rb, h);
   store_tile(y, M, N, tm, tn, wave, lr, h, 1.0f, acc);
 }
 
