@@ -30,10 +30,10 @@ __device__ __forceinline__ void dequant_chunk(const uint8_t* __restrict__ data,
     const f32x2 e0 = cvt_pk_f32_fp4<0>(q), e1 = cvt_pk_f32_fp4<1>(q);
     const f32x2 e2 = cvt_pk_f32_fp4<2>(q), e3 = cvt_pk_f32_fp4<3>(q);
     uint4 o;
-    o.x = f32_to_bf16_rne(e0.x * d) | (f32_to_bf16_rne(e0.y * d) << 16);
-    o.y = f32_to_bf16_rne(e1.x * d) | (f32_to_bf16_rne(e1.y * d) << 16);
-    o.z = f32_to_bf16_rne(e2.x * d) | (f32_to_bf16_rne(e2.y * d) << 16);
-    o.w = f32_to_bf16_rne(e3.x * d) | (f32_to_bf16_rne(e3.y * d) << 16);
+    o.x = pack_bf16x2(e0.x * d, e0.y * d);
+    o.y = pack_bf16x2(e1.x * d, e1.y * d);
+    o.z = pack_bf16x2(e2.x * d, e2.y * d);
+    o.w = pack_bf16x2(e3.x * d, e3.y * d);
     reinterpret_cast<uint4*>(out)[g] = o;
   } else {
     // 4 values = one 2-byte half-word of nibbles; block g/4
@@ -80,10 +80,10 @@ __device__ __forceinline__ void store_values(void* out, int64_t b, const float (
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 w;
-      w.x = f32_to_bf16_rne(v[8 * h + 0]) | (f32_to_bf16_rne(v[8 * h + 1]) << 16);
-      w.y = f32_to_bf16_rne(v[8 * h + 2]) | (f32_to_bf16_rne(v[8 * h + 3]) << 16);
-      w.z = f32_to_bf16_rne(v[8 * h + 4]) | (f32_to_bf16_rne(v[8 * h + 5]) << 16);
-      w.w = f32_to_bf16_rne(v[8 * h + 6]) | (f32_to_bf16_rne(v[8 * h + 7]) << 16);
+      w.x = pack_bf16x2(v[8 * h + 0], v[8 * h + 1]);
+      w.y = pack_bf16x2(v[8 * h + 2], v[8 * h + 3]);
+      w.z = pack_bf16x2(v[8 * h + 4], v[8 * h + 5]);
+      w.w = pack_bf16x2(v[8 * h + 6], v[8 * h + 7]);
       o[h] = w;
     }
   } else {

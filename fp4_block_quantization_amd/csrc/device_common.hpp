@@ -74,6 +74,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Two finite fp32 values -> packed bf16 (a in the low half), nearest-even, with the
+// hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // ---- E4M3 (OCP "FN": bias 7, max 448) ------------------------------------------
 // Round r >= 0 (or +inf) to the nearest E4M3 value, ties to even, saturating to 448.
 __device__ __forceinline__ uint32_t e4m3_encode(float r) {

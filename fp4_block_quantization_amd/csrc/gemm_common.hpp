@@ -52,7 +52,6 @@ __device__ __forceinline__ TileCoord tile_of(int w, int tiles_m, int tiles_n) {
 __device__ __forceinline__ void store_tile_full(uint16_t* y, int M, int N, int m0, int n0,
                                                 int lr, int h, float s,
                                                 const f32x16 (&acc)[4][4]) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
       (void*)y, 0, (int)((uint32_t)M * (uint32_t)N * 2u), kRsrcWord3);
   const int odd = lr & 1;
@@ -66,8 +65,7 @@ __device__ __forceinline__ void store_tile_full(uint16_t* y, int M, int N, int m
                             (uint32_t)(n0 + 32 * n + lr - odd) * 2u;
 #pragma unroll
       for (int a = 0; a < 16; a += 2) {
-        const f32x2 v = {acc[i][n][a] * s, acc[i][n][a + 1] * s};
-        const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        const uint32_t p = pack_bf16x2(acc[i][n][a] * s, acc[i][n][a + 1] * s);
         const uint32_t q = __builtin_amdgcn_update_dpp(0u, p, 0xB1, 0xF, 0xF, false);
         const uint32_t out = __builtin_amdgcn_perm(q, p, sel);
         const int drow = (a & 3) + 8 * (a >> 2);

@@ -109,10 +109,10 @@ __device__ __forceinline__ void mx_dequant_chunk(const uint8_t* __restrict__ dat
     const f32x2 e0 = cvt_pk_f32_fp4<0>(q), e1 = cvt_pk_f32_fp4<1>(q);
     const f32x2 e2 = cvt_pk_f32_fp4<2>(q), e3 = cvt_pk_f32_fp4<3>(q);
     uint4 o;
-    o.x = f32_to_bf16_rne(e0.x * d) | (f32_to_bf16_rne(e0.y * d) << 16);
-    o.y = f32_to_bf16_rne(e1.x * d) | (f32_to_bf16_rne(e1.y * d) << 16);
-    o.z = f32_to_bf16_rne(e2.x * d) | (f32_to_bf16_rne(e2.y * d) << 16);
-    o.w = f32_to_bf16_rne(e3.x * d) | (f32_to_bf16_rne(e3.y * d) << 16);
+    o.x = pack_bf16x2(e0.x * d, e0.y * d);
+    o.y = pack_bf16x2(e1.x * d, e1.y * d);
+    o.z = pack_bf16x2(e2.x * d, e2.y * d);
+    o.w = pack_bf16x2(e3.x * d, e3.y * d);
     reinterpret_cast<uint4*>(out)[g] = o;
   } else {
     // 4 values = one 2-byte half-word of nibbles; block g/8
