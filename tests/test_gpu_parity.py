@@ -484,3 +484,18 @@ def test_qlinear_with_hadamard_on_both_operands(fos):
     exact = F.bf16_bits_to_f32(xb).astype(np.float64) @ F.bf16_bits_to_f32(wb).astype(np.float64).T
     got = F.bf16_bits_to_f32(y).astype(np.float64)
     assert np.linalg.norm(got - exact) / np.linalg.norm(exact) < 0.15
+
+
+def test_gemms_are_deterministic(fos):
+    """Repeated GEMM calls give bit-identical outputs (fixed accumulation order; no
+    atomics or split-K)."""
+    xb = bits_of(W.random_bf16(512, 1024, 81, "student_t"))
+    wb = bits_of(W.random_bf16(768, 1024, 83, "normal", scale=0.02))
+    x, w = to_gpu_bf16(xb), to_gpu_bf16(wb)
+    xq, wq = fos.quantize(x), fos.quantize(w)
+    ma, mb = fos.mx_quantize(x), fos.mx_quantize(w)
+    a = [fos.qlinear_fwd(xq, wq) for _ in range(3)]
+    b = [fos.mx_qlinear_fwd(ma, mb) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(a[0], t) for t in a[1:])
+    assert all(torch.equal(b[0], t) for t in b[1:])
