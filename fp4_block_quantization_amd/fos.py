@@ -208,6 +208,25 @@ def _check_input(x: torch.Tensor):
         raise ValueError("x must be a contiguous 2-D bfloat16 CUDA tensor")
 
 
+def _check_record(q, *others):
+    """A record's tensors must be contiguous CUDA tensors on one device (the library
+    dereferences them on the GPU), with the shapes the layout implies."""
+    dev = q.data.device
+    tensors = [q.data, q.scales] + ([q.tensor_scale] if hasattr(q, "tensor_scale") else [])
+    for o in others:
+        tensors += [o.data, o.scales] + ([o.tensor_scale] if hasattr(o, "tensor_scale") else [])
+    for t in tensors:
+        if not t.is_cuda or t.device != dev or not t.is_contiguous():
+            raise ValueError("record tensors must be contiguous CUDA tensors on one device")
+    for r in (q,) + others:
+        if r.data.dtype != torch.uint8 or r.scales.dtype != torch.uint8 or r.data.dim() != 2:
+            raise ValueError("record data and scales must be 2-D uint8 tensors")
+        block = 32 if not hasattr(r, "tensor_scale") else 16
+        R, C = r.shape
+        if tuple(r.scales.shape) != (R, C // block):
+            raise ValueError(f"scales must be [{R}, {C // block}]")
+
+
 def tensor_scale(x: torch.Tensor, hadamard_seed: Optional[int] = None,
                  outputs: Sequence[str] = ("row",)) -> torch.Tensor:
     _check_input(x)
@@ -252,6 +271,7 @@ def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.float32,
                inverse_hadamard: bool = False) -> torch.Tensor:
     """Dequantize a record ([R, C] as stored).  With ``inverse_hadamard`` a record made
     with the random Hadamard transform is returned to the original basis."""
+    _check_record(q)
     R, C = q.shape
     out = torch.empty(R, C, dtype=dtype, device=q.data.device)
     if inverse_hadamard:
@@ -269,6 +289,7 @@ def qlinear_fwd(xq: NVFP4Tensor, wq: NVFP4Tensor, out: Optional[torch.Tensor] = 
     dimension: A [M, K], B [N, K] as stored (a column-wise record of W is the record
     of W^T; 2D records carry one scale per 16 values too).  ``out``: optional bf16
     [M, N] destination."""
+    _check_record(xq, wq)
     M, K = xq.shape
     N, K2 = wq.shape
     if K != K2:
@@ -292,6 +313,8 @@ def qlinear_bwd(dyq: Optional[NVFP4Tensor], dyq_t: Optional[NVFP4Tensor],
     W^T [K, N])."""
     if not (need_dx or need_dw):
         raise ValueError("nothing to compute")
+    used = ([dyq, wq_t] if need_dx else []) + ([dyq_t, xq_t] if need_dw else [])
+    _check_record(*used)
     if need_dx:
         M, N = dyq.shape
         K, N2 = wq_t.shape
@@ -341,6 +364,7 @@ def mx_quantize(x: torch.Tensor) -> MXFP4Tensor:
 
 
 def mx_dequantize(q: MXFP4Tensor, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    _check_record(q)
     R, C = q.shape
     out = torch.empty(R, C, dtype=dtype, device=q.data.device)
     dt = {torch.float32: FOS_OUT_F32, torch.bfloat16: FOS_OUT_BF16}[dtype]
@@ -352,6 +376,7 @@ def mx_dequantize(q: MXFP4Tensor, dtype: torch.dtype = torch.float32) -> torch.T
 def mx_qlinear_fwd(aq: MXFP4Tensor, bq: MXFP4Tensor, out: Optional[torch.Tensor] = None
                    ) -> torch.Tensor:
     """Y = deq(A) deq(B)^T in bf16 on the FP4 matrix cores; A [M, K], B [N, K]."""
+    _check_record(aq, bq)
     M, K = aq.shape
     N, K2 = bq.shape
     if K != K2:

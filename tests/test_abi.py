@@ -159,3 +159,17 @@ def test_tensor_scale_validation():
     assert L.fos_tensor_scale(ctypes.byref(c), FAKE, 16, 32, FAKE, FAKE, 8, None) == fos.FOS_E_WORKSPACE
     c2 = cfg(outputs=("col",), hadamard_seed=3)
     assert L.fos_tensor_scale(ctypes.byref(c2), FAKE, 24, 32, FAKE, FAKE, 1 << 14, None) == fos.FOS_E_SHAPE
+
+
+def test_binding_rejects_host_records():
+    """A record on the host would hand host addresses to the GPU: the binding refuses."""
+    import torch
+    q = fos.NVFP4Tensor(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8),
+                        torch.zeros(1))
+    with pytest.raises(ValueError):
+        fos.qlinear_fwd(q, q)
+    with pytest.raises(ValueError):
+        fos.dequantize(q)
+    m = fos.MXFP4Tensor(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 1, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        fos.mx_qlinear_fwd(m, m)
