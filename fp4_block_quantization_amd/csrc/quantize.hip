@@ -6,15 +6,18 @@
 // Three kernels, all one-pass over the bf16 input with every 16-value block held in
 // one lane's registers while both candidates are evaluated:
 //   quant_rows_kernel  row-wise 1D output: the tensor is a flat run of 16-value
-//                      blocks; lane = block; two 16-byte loads, one 8-byte store of
-//                      nibbles and one scale byte per lane.
+//                      blocks; lane = two blocks; two 16-byte loads, one 8-byte store
+//                      of nibbles and one scale byte per block.
 //   quant_tile_kernel  column-wise output (optionally row-wise from the same read):
-//                      a 256x64 tile goes through LDS (XOR-swizzled 16-byte groups,
-//                      so column reads hit 32 distinct banks per wave); each lane then
+//                      a 128x64 tile goes through LDS (XOR-swizzled 16-byte groups,
+//                      so the column reads spread over the banks); each lane then
 //                      reads two adjacent 16-row column blocks as 16 dwords.
-//   quant_2d_kernel    16x16 tiles: 16 lanes hold the 16 rows of a tile; tile max and
-//                      error sums use lane shuffles; column-wise output is the LDS
-//                      transpose of the same nibbles.
+//   quant_2d_kernel    16x16 tiles: the 16 lanes of a DPP row hold the 16 rows of a
+//                      tile (two tile rows per workgroup); tile max and error sums use
+//                      DPP row permutes; column-wise output is the LDS transpose of the
+//                      same nibbles.
+// Every workgroup first finishes the tensor scale (from the scale pass's partial
+// maxima, or the caller's t) and builds a table of (d, 1/d) for all E4M3 codes.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
