@@ -314,6 +314,57 @@ def cpu_baseline(x_cpu, rows_sample):
                       f"{dt:.1f} s of single-threaded NumPy"}
 
 
+_MC_BITS = None
+
+
+def _mc_quantize(args):
+    import numpy as np
+    from oracle import nvfp4 as N
+    lo, hi, t = args
+    N.quantize(_MC_BITS[lo:hi], N.Config(), t=np.float32(t))
+    return hi - lo
+
+
+def cpu_baselines_extra(x_cpu, x5_cpu, w5_cpu, workers):
+    """Reported CPU baselines beside the single-core one: the oracle row-chunked over
+    `workers` processes (tensor scale in the parent), and the pages' own fallback for
+    the quantized linear, an fp32 matmul over dequantized operands on the CPU."""
+    import multiprocessing as mp
+    import numpy as np
+    import torch
+    from oracle import nvfp4 as N
+    global _MC_BITS
+    bits = x_cpu.contiguous().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    _, t = N.prepare(bits, N.Config())
+    _MC_BITS = bits
+    R = bits.shape[0]
+    edges = np.linspace(0, R, 4 * workers + 1).astype(int)
+    with mp.get_context("fork").Pool(workers) as pool:
+        done = sum(pool.map(_mc_quantize, [(int(a), int(b), float(t)) for a, b in zip(edges[:-1], edges[1:])]))
+    dt = time.perf_counter() - t0
+    assert done == R
+    b = quant_bytes(R, bits.shape[1])
+    mc = {"value": b / dt / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+          "sample": f"oracle quantize of the whole 4096x12288 weight, row chunks over {workers} "
+                    f"processes, {dt:.1f} s"}
+    # fp32 matmul fallback on a 1024-row slice of X against all of W (c5 shapes; the
+    # operand values do not change the time of a dense fp32 matmul)
+    xs = x5_cpu[:1024].float().contiguous()
+    ws = w5_cpu.float().contiguous()
+    torch.matmul(xs[:64], ws.T)
+    t0 = time.perf_counter()
+    reps = 3
+    for _ in range(reps):
+        torch.matmul(xs, ws.T)
+    dt = (time.perf_counter() - t0) / reps
+    flops = 2 * xs.shape[0] * ws.shape[0] * xs.shape[1]
+    mm = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+          "kind": "fp32 matmul (the pages' CPU fallback)",
+          "sample": f"torch.matmul fp32 [1024, 4096] x [4096, 12288] on the CPU, {dt * 1e3:.0f} ms"}
+    return mc, mm
+
+
 def traffic_for(kernel: str):
     try:
         rec = json.load(open(PMC_FILE))[kernel]
@@ -341,10 +392,23 @@ def main():
         sys.exit(2)
 
     import torch
-    from fp4_block_quantization_amd import fos, workloads as W
+    from fp4_block_quantization_amd import workloads as W
 
-    log(f"device: {torch.cuda.get_device_name(0)}")
     x2 = W.make("c2")
+    # CPU baselines first, before anything touches the GPU: the multi-process one forks
+    # workers, which must not inherit an initialised GPU runtime.
+    cpu = None
+    cpu_rows = {}
+    if not args.no_cpu and args.only is None:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline(x2, x2.shape[0])
+        workers = max(1, min(8, os.cpu_count() or 1))
+        log(f"CPU oracle on {workers} processes, CPU fp32 matmul ...")
+        mc, mm = cpu_baselines_extra(x2, W.make("c5_x"), W.make("c5_w"), workers)
+        cpu_rows = {"cpu_oracle_multicore": mc, "cpu_fp32_matmul_c5_slice": mm}
+
+    from fp4_block_quantization_amd import fos
+    log(f"device: {torch.cuda.get_device_name(0)}")
 
     if args.only is not None:
         if args.only == "c5_qlinear":
@@ -426,10 +490,7 @@ def main():
     rows["mxfp4"] = bench_mx(fos, W.make("c5_x"), W.make("c5_w"), x2, args.steps, args.warmup)
     log(json.dumps(rows["mxfp4"]))
 
-    cpu = None
-    if not args.no_cpu:
-        log("CPU oracle baseline ...")
-        cpu = cpu_baseline(x2, x2.shape[0])
+    rows.update(cpu_rows)
 
     kernel_gbps = head["GBps_quant_kernel"]
     out = {
