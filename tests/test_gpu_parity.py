@@ -499,3 +499,31 @@ def test_gemms_are_deterministic(fos):
     torch.cuda.synchronize()
     assert all(torch.equal(a[0], t) for t in a[1:])
     assert all(torch.equal(b[0], t) for t in b[1:])
+
+
+def _random_case(i):
+    """Seeded random configuration i: any valid option combination, shape and range."""
+    rng = np.random.default_rng(1000 + i)
+    block = "2d" if rng.random() < 0.25 else "1d"
+    had = block == "1d" and rng.random() < 0.4
+    if had:
+        outs = [("row", "col")[rng.integers(2)]]
+    else:
+        outs = [("row",), ("col",), ("row", "col")][rng.integers(3)]
+    rows = 16 * int(rng.integers(1, 24)) if ("col" in outs or block == "2d") else int(rng.integers(1, 300))
+    cols = 16 * int(rng.integers(1, 90))
+    cfg = N.Config(rule=("4/6", "6")[int(rng.random() < 0.2)],
+                   rounding=("rne", "sr")[int(rng.random() < 0.4)], block=block,
+                   rows_out="row" in outs, cols_out="col" in outs, hadamard=had,
+                   hadamard_seed=int(rng.integers(0, 2 ** 63)),
+                   sr_seed=int(rng.integers(0, 2 ** 63)))
+    scale = float(10.0 ** rng.uniform(-30, 20))
+    dist = ("normal", "student_t", "uniform")[rng.integers(3)]
+    return rows, cols, cfg, scale, dist, int(rng.integers(0, 2 ** 31))
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_configurations_match_oracle(fos, i):
+    rows, cols, cfg, scale, dist, seed = _random_case(i)
+    bits = bits_of(W.random_bf16(rows, cols, seed, dist, scale=scale))
+    assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
