@@ -60,6 +60,19 @@ __device__ __forceinline__ void store_block(uint8_t* data, uint8_t* scales, int6
   scales[scale_off] = (uint8_t)c.s;
 }
 
+// The same with non-temporal stores, for kernels whose workgroups write whole runs of
+// consecutive blocks (the row-wise kernel): the outputs are written once and not read
+// back, and keeping them out of the caches measurably shortens the quantize step.
+// Kernels that write scattered pieces of lines (tile, 2D) keep the cached stores,
+// which let L2 merge the pieces.
+__device__ __forceinline__ void store_block_stream(uint8_t* data, uint8_t* scales,
+                                                   int64_t data_off, int64_t scale_off,
+                                                   const Cand& c) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(v2u{c.lo, c.hi}, reinterpret_cast<v2u*>(data + data_off));
+  __builtin_nontemporal_store((uint8_t)c.s, scales + scale_off);
+}
+
 // ------------------------------------------------------------------ row-wise, 1D
 // Each lane owns blocks b and b + 256 of its workgroup's 512; both blocks' four
 // 16-byte loads are issued before either is quantized.
@@ -76,8 +89,13 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
     w[2 * q] = make_uint4(0, 0, 0, 0);
     w[2 * q + 1] = w[2 * q];
     if (b < nblk) {
-      w[2 * q] = x[2 * b];
-      w[2 * q + 1] = x[2 * b + 1];
+      // input read once: non-temporal loads
+      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+      const v4u* xv = reinterpret_cast<const v4u*>(x);
+      const v4u l0 = __builtin_nontemporal_load(xv + 2 * b);
+      const v4u l1 = __builtin_nontemporal_load(xv + 2 * b + 1);
+      w[2 * q] = make_uint4(l0.x, l0.y, l0.z, l0.w);
+      w[2 * q + 1] = make_uint4(l1.x, l1.y, l1.z, l1.w);
     }
   }
   __shared__ float2 tab[kScaleTableSize];
@@ -92,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
     float srq[16];
     if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srq);
     const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
-    store_block(a.row_data, a.row_scales, 8 * b, b, c);
+    store_block_stream(a.row_data, a.row_scales, 8 * b, b, c);
   }
 }
 
