@@ -17,6 +17,11 @@ namespace fos {
 namespace {
 
 constexpr int kThreads = 256;
+
+// The output-major kernel's outputs are written once, 1 KB contiguous per wave
+// instruction: non-temporal 16-byte stores (measured faster than cached ones).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kUnroll = 4;
 
 template <bool kBF16>
@@ -34,13 +39,14 @@ __device__ __forceinline__ void dequant_chunk(const uint8_t* __restrict__ data,
     o.y = pack_bf16x2(e1.x * d, e1.y * d);
     o.z = pack_bf16x2(e2.x * d, e2.y * d);
     o.w = pack_bf16x2(e3.x * d, e3.y * d);
-    reinterpret_cast<uint4*>(out)[g] = o;
+    __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out) + g);
   } else {
     // 4 values = one 2-byte half-word of nibbles; block g/4
     const uint32_t q = reinterpret_cast<const uint16_t*>(data)[g];
     const float d = e4m3_decode(scales[g >> 2]) * t;
     const f32x2 e0 = cvt_pk_f32_fp4<0>(q), e1 = cvt_pk_f32_fp4<1>(q);
-    reinterpret_cast<float4*>(out)[g] = make_float4(e0.x * d, e0.y * d, e1.x * d, e1.y * d);
+    __builtin_nontemporal_store(v4f{e0.x * d, e0.y * d, e1.x * d, e1.y * d},
+                                reinterpret_cast<v4f*>(out) + g);
   }
 }
 
@@ -75,17 +81,14 @@ __device__ __forceinline__ void dequant_block(uint2 q, uint32_t s, float t, floa
 // Store block b's 16 values: 32 bytes of bf16 (RNE) or 64 bytes of fp32.
 template <bool kBF16>
 __device__ __forceinline__ void store_values(void* out, int64_t b, const float (&v)[16]) {
+  // cached stores: each instruction writes 16 bytes at a 32- or 64-byte stride, and L2
+  // merges the pieces of a line (non-temporal stores measured slower here)
   if (kBF16) {
     uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 w;
-      w.x = pack_bf16x2(v[8 * h + 0], v[8 * h + 1]);
-      w.y = pack_bf16x2(v[8 * h + 2], v[8 * h + 3]);
-      w.z = pack_bf16x2(v[8 * h + 4], v[8 * h + 5]);
-      w.w = pack_bf16x2(v[8 * h + 6], v[8 * h + 7]);
-      o[h] = w;
-    }
+    for (int h = 0; h < 2; ++h)
+      o[h] = make_uint4(pack_bf16x2(v[8 * h + 0], v[8 * h + 1]), pack_bf16x2(v[8 * h + 2], v[8 * h + 3]),
+                        pack_bf16x2(v[8 * h + 4], v[8 * h + 5]), pack_bf16x2(v[8 * h + 6], v[8 * h + 7]));
   } else {
     float4* o = reinterpret_cast<float4*>(out) + 4 * b;
 #pragma unroll

@@ -29,6 +29,11 @@ using namespace gemm;
 
 constexpr int kThreads = 256;
 
+// Outputs are written once: non-temporal stores.  (The input stays on cached loads: a
+// lane's four 16-byte loads are 64 bytes apart across the wave, and uncached they
+// would fetch the shared lines more than once.)
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------------ quantize
 
 // Shared exponent from the block maximum's fp32 pattern: floor(log2 a) = exponent
@@ -84,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint4* __restr
       r = cvt_pk_fp4<3>(r, v[8 * k + 6] * inv, v[8 * k + 7] * inv);
       o[k] = r;
     }
-    reinterpret_cast<uint4*>(data)[b] = make_uint4(o[0], o[1], o[2], o[3]);
-    scales[b] = (uint8_t)(e + 127);
+    __builtin_nontemporal_store(v4u{o[0], o[1], o[2], o[3]}, reinterpret_cast<v4u*>(data) + b);
+    __builtin_nontemporal_store((uint8_t)(e + 127), scales + b);
   }
 }
 
