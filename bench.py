@@ -265,6 +265,16 @@ def bench_mx(fos, x_cpu, w_cpu, x2_cpu, steps, warmup):
         bad[0] |= f(*args[i])
     ms_q = time_loop(fq, steps, warmup, sets)
     qb = 2 * R * C + R * C // 2 + R * C // 32
+    outs16 = [torch.empty(R, C, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    dargs = [(_vp(outs[i][0]), _vp(outs[i][1]), R, C, fos.FOS_OUT_BF16, _vp(outs16[i]), stream)
+             for i in range(sets)]
+    fd_ = lib.fos_mx_dequantize
+
+    def fd(i):
+        bad[0] |= fd_(*dargs[i])
+    ms_d = time_loop(fd, steps, warmup, sets)
+    db = R * C // 2 + R * C // 32 + 2 * R * C
+    del outs16
     aq = fos.mx_quantize(x_cpu.to(dev))
     bq = fos.mx_quantize(w_cpu.to(dev))
     M, K = aq.shape
@@ -281,6 +291,8 @@ def bench_mx(fos, x_cpu, w_cpu, x2_cpu, steps, warmup):
     flops = 2 * M * N * K
     return {"quantize_c2": {"bytes": qb, "ms": ms_q, "GBps": qb / ms_q / 1e6,
                             "frac": qb / ms_q / 1e6 / HBM_PEAK_GBS},
+            "dequantize_c2_bf16": {"bytes": db, "ms": ms_d, "GBps": db / ms_d / 1e6,
+                                   "frac": db / ms_d / 1e6 / HBM_PEAK_GBS},
             "gemm_c5": {"shape": [M, N, K], "flop": flops, "ms": ms_g, "TFLOPs": flops / ms_g / 1e9,
                         "frac_fp4_peak": flops / ms_g / 1e9 / FP4_MFMA_PEAK_TFLOPS}}
 

@@ -118,13 +118,15 @@ __device__ __forceinline__ void mx_dequant_chunk(const uint8_t* __restrict__ dat
     o.y = pack_bf16x2(e1.x * d, e1.y * d);
     o.z = pack_bf16x2(e2.x * d, e2.y * d);
     o.w = pack_bf16x2(e3.x * d, e3.y * d);
-    reinterpret_cast<uint4*>(out)[g] = o;
+    __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out) + g);
   } else {
     // 4 values = one 2-byte half-word of nibbles; block g/8
     const uint32_t q = reinterpret_cast<const uint16_t*>(data)[g];
     const float d = e8m0_value(scales[g >> 3]);
     const f32x2 e0 = cvt_pk_f32_fp4<0>(q), e1 = cvt_pk_f32_fp4<1>(q);
-    reinterpret_cast<float4*>(out)[g] = make_float4(e0.x * d, e0.y * d, e1.x * d, e1.y * d);
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(v4f{e0.x * d, e0.y * d, e1.x * d, e1.y * d},
+                                reinterpret_cast<v4f*>(out) + g);
   }
 }
 
