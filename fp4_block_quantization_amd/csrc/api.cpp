@@ -132,6 +132,7 @@ fos_status check_gemm(const uint8_t* a_data, const uint8_t* a_scales, const floa
   // each packed operand is addressed through one buffer resource (< 4 GiB)
   if ((M + 256) * (K / 2) >= ((int64_t)1 << 32) || (N + 256) * (K / 2) >= ((int64_t)1 << 32))
     return FOS_E_SHAPE;
+  if (fos::qlinear_grid(M, N) > fos::kMaxGrid) return FOS_E_SHAPE;
   if (!a_data || !a_scales || !a_t || !b_data || !b_scales || !b_t || !y) return FOS_E_NULL;
   if (!aligned(a_data, 16) || !aligned(b_data, 16) || !aligned(a_scales, 4) ||
       !aligned(b_scales, 4) || !aligned(y, 2) || !aligned(a_t, 4) || !aligned(b_t, 4))
@@ -207,6 +208,7 @@ fos_status fos_quantize_scaled(const fos_quant_config* cfg, const void* x, int64
     return st;
   const fos::QuantArgs a =
       make_args(cfg, x, rows, cols, tensor_scale, row_data, row_scales, col_data, col_scales);
+  if (fos::quantize_grid(a) > fos::kMaxGrid) return FOS_E_SHAPE;
   return fos::launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FOS_OK
                                                                                  : FOS_E_HIP;
 }
@@ -222,6 +224,9 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
     return st;
   if ((st = check_outputs(cfg, rows, cols, row_data, row_scales, col_data, col_scales)) != FOS_OK)
     return st;
+  fos::QuantArgs a =
+      make_args(cfg, x, rows, cols, nullptr, row_data, row_scales, col_data, col_scales);
+  if (fos::quantize_grid(a) > fos::kMaxGrid) return FOS_E_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // an empty tensor launches no quantize kernel: the scale pass writes t (= 0) itself
   const bool empty = rows * cols == 0;
@@ -230,8 +235,6 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
       FOS_OK)
     return st;
   if (empty) return FOS_OK;
-  fos::QuantArgs a =
-      make_args(cfg, x, rows, cols, nullptr, row_data, row_scales, col_data, col_scales);
   a.partials = static_cast<const float*>(workspace);
   a.npartials = npartials;
   a.tscale_out = tensor_scale;
@@ -303,6 +306,7 @@ fos_status fos_mx_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* d
   if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return FOS_E_SHAPE;
   if (rows > 0 && cols > kMaxElems / rows) return FOS_E_SHAPE;
   if (cols % 32) return FOS_E_SHAPE;
+  if (fos::mx_quantize_grid(rows, cols) > fos::kMaxGrid) return FOS_E_SHAPE;
   if (rows * cols == 0) return FOS_OK;
   if (!x || !data || !scales) return FOS_E_NULL;
   if (!aligned(x, 16) || !aligned(data, 16)) return FOS_E_ALIGN;
@@ -335,6 +339,7 @@ fos_status fos_mx_qlinear_fwd(const uint8_t* a_data, const uint8_t* a_scales,
   if (N > kMaxElems / M || K > kMaxElems / M || K > kMaxElems / N) return FOS_E_SHAPE;
   if ((M + 256) * (K / 2) >= ((int64_t)1 << 32) || (N + 256) * (K / 2) >= ((int64_t)1 << 32))
     return FOS_E_SHAPE;
+  if (fos::mx_gemm_grid(M, N) > fos::kMaxGrid) return FOS_E_SHAPE;
   if (!a_data || !a_scales || !b_data || !b_scales || !y_bf16) return FOS_E_NULL;
   if (!aligned(a_data, 16) || !aligned(b_data, 16) || !aligned(a_scales, 4) ||
       !aligned(b_scales, 4) || !aligned(y_bf16, 2))

@@ -35,6 +35,14 @@ hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bo
                                bool finalize, float* tscale, int* npartials,
                                hipStream_t stream);
 
+// One dispatch covers at most 2^32 - 1 work-items along a grid dimension, so a launch
+// of 256-thread workgroups may use at most this many workgroups.  The C ABI checks
+// the grid of every launch below against it before launching anything.
+constexpr int64_t kMaxGrid = (((int64_t)1 << 32) - 1) / 256;
+
+// Workgroups of the quantize launch for these arguments (0 for an empty tensor).
+int64_t quantize_grid(const QuantArgs& a);
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
@@ -50,6 +58,8 @@ hipError_t launch_dequantize_hadamard(const uint8_t* data, const uint8_t* scales
 
 // MXFP4 (32 E2M1 values per E8M0 scale): quantize bf16 [rows][cols] (cols % 32 == 0),
 // dequantize, and the native FP4 GEMM Y = deq(A) deq(B)^T (K % 256 == 0).
+int64_t mx_quantize_grid(int64_t rows, int64_t cols);
+int64_t mx_gemm_grid(int64_t M, int64_t N);
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* data,
                               uint8_t* scales, hipStream_t stream);
 hipError_t launch_mx_dequantize(const uint8_t* data, const uint8_t* scales, int64_t rows,
@@ -57,6 +67,9 @@ hipError_t launch_mx_dequantize(const uint8_t* data, const uint8_t* scales, int6
 hipError_t launch_mx_gemm(const uint8_t* ad, const uint8_t* as, const uint8_t* bd,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, uint16_t* y,
                           hipStream_t stream);
+
+// Workgroups of the qlinear launch for an [M][N] output.
+int64_t qlinear_grid(int64_t M, int64_t N);
 
 hipError_t launch_qlinear(const uint8_t* xd, const uint8_t* xs, const float* xt,
                           const uint8_t* wd, const uint8_t* ws, const float* wt, int64_t M,

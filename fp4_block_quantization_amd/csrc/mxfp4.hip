@@ -315,11 +315,19 @@ void mx_gemm_kernel(const uint8_t* __restrict__ ad, const uint8_t* __restrict__ 
 
 }  // namespace
 
+int64_t mx_quantize_grid(int64_t rows, int64_t cols) {
+  return (rows * cols / 32 + kMxBlocksPerWG - 1) / kMxBlocksPerWG;
+}
+
+int64_t mx_gemm_grid(int64_t M, int64_t N) {
+  return ((M + kMxTile - 1) / kMxTile) * ((N + kMxTile - 1) / kMxTile);
+}
+
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* data,
                               uint8_t* scales, hipStream_t s) {
   const int64_t nblk = rows * cols / 32;
   if (nblk == 0) return hipSuccess;
-  const int64_t grid = (nblk + kMxBlocksPerWG - 1) / kMxBlocksPerWG;
+  const int64_t grid = mx_quantize_grid(rows, cols);
   mx_quant_kernel<<<grid, kThreads, 0, s>>>((const uint4*)x, nblk, data, scales);
   return hipGetLastError();
 }

@@ -471,6 +471,12 @@ hipError_t launch_cfg(const uint8_t* xd, const uint8_t* xs, const float* xt, con
 
 }  // namespace
 
+// Both kernels tile the output in 256 x 256 blocks (launch_cfg<4, 4, ...>: 64 * 4).
+int64_t qlinear_grid(int64_t M, int64_t N) {
+  static_assert(64 * 4 == kTileRows, "both qlinear kernels use the same output tile");
+  return ((M + kTileRows - 1) / kTileRows) * ((N + kTileRows - 1) / kTileRows);
+}
+
 hipError_t launch_qlinear(const uint8_t* xd, const uint8_t* xs, const float* xt,
                           const uint8_t* wd, const uint8_t* ws, const float* wt, int64_t M,
                           int64_t N, int64_t K, uint16_t* y, hipStream_t s) {

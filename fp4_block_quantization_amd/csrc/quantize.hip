@@ -304,9 +304,7 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
 
 template <bool k46, bool kSR>
 hipError_t dispatch_2d(const QuantArgs& a, hipStream_t s) {
-  const int64_t tiles_c = a.cols / 16;
-  const int64_t tile_rows = a.rows / 16;
-  const int64_t grid = ((tile_rows + k2dTileRows - 1) / k2dTileRows) * ((tiles_c + 15) / 16);
+  const int64_t grid = quantize_grid(a);
   if (a.rows_out && a.cols_out)
     quant_2d_kernel<k46, kSR, true, true><<<grid, kThreads, 0, s>>>(a);
   else if (a.rows_out)
@@ -318,14 +316,12 @@ hipError_t dispatch_2d(const QuantArgs& a, hipStream_t s) {
 
 template <bool k46, bool kSR, bool kRHT>
 hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
+  const int64_t grid = quantize_grid(a);
   if (!a.cols_out) {
-    const int64_t nblk = a.rows * a.cols / 16;
-    const int64_t grid = (nblk + kRowsPerWG - 1) / kRowsPerWG;
-    quant_rows_kernel<k46, kSR, kRHT><<<grid, kThreads, 0, s>>>(a, nblk);
+    quant_rows_kernel<k46, kSR, kRHT><<<grid, kThreads, 0, s>>>(a, a.rows * a.cols / 16);
     return hipGetLastError();
   }
   constexpr int TR = kColTileRows;
-  const int64_t grid = ((a.rows + TR - 1) / TR) * ((a.cols + kTileC - 1) / kTileC);
   if (a.rows_out)
     quant_tile_kernel<TR, k46, kSR, kRHT, true><<<grid, kThreads, 0, s>>>(a);
   else
@@ -340,6 +336,14 @@ hipError_t dispatch_rule(const QuantArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int64_t quantize_grid(const QuantArgs& a) {
+  if (a.rows == 0 || a.cols == 0) return 0;
+  if (a.two_d)  // k2dTileRows tile rows x 16 tile columns per workgroup
+    return ((a.rows / 16 + k2dTileRows - 1) / k2dTileRows) * ((a.cols / 16 + 15) / 16);
+  if (!a.cols_out) return (a.rows * a.cols / 16 + kRowsPerWG - 1) / kRowsPerWG;
+  return ((a.rows + kColTileRows - 1) / kColTileRows) * ((a.cols + kTileC - 1) / kTileC);
+}
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;

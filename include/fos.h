@@ -48,8 +48,11 @@ extern "C" {
 typedef enum {
   FOS_OK = 0,
   FOS_E_NULL = 1,      /* a required pointer is NULL                                */
-  FOS_E_SHAPE = 2,     /* negative size, or a size that must be a multiple of 16
-                          (or of 64 for the qlinear K) is not                       */
+  FOS_E_SHAPE = 2,     /* negative size, a size that must be a multiple of 16 (or
+                          of 32, 64, 256 where stated) is not, a dimension of 2^31
+                          or more, more than 2^40 elements in one tensor, or a
+                          shape whose launch would need more than 2^32 - 1
+                          work-items (e.g. 2D blocks on a [2^29, 16] tensor)       */
   FOS_E_ALIGN = 3,     /* bf16 input not 16-byte aligned, packed data not 8-byte
                           aligned, or an output buffer misaligned                   */
   FOS_E_FLAGS = 4,     /* unknown enum value, wrong struct_size, or an unsupported

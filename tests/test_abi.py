@@ -80,6 +80,24 @@ def test_quantize_validation(kw, args, want):
     assert q(cfg(**kw), **args) == want
 
 
+def test_launch_grid_limit():
+    """Shapes whose launch would exceed 2^32 - 1 work-items are rejected up front, with
+    no kernel (not even the tensor-scale pass) launched."""
+    L = fos.lib()
+    f = FAKE
+    # 2D tiles: (2^25 - 1) tile rows / 2 per workgroup -> 2^24 workgroups of 256
+    assert q(cfg(block="2d"), rows=(1 << 29) - 16, cols=16) == fos.FOS_E_SHAPE
+    # column-wise 128 x 64 tiles of a [2^31 - 16, 16] tensor -> 2^24 workgroups
+    assert q(cfg(outputs=("col",)), rows=(1 << 31) - 16, cols=16) == fos.FOS_E_SHAPE
+    t = ctypes.byref(cfg(outputs=("col",)))
+    assert L.fos_quantize_scaled(t, f, (1 << 31) - 16, 16, f, f, f, f, f, None) == fos.FOS_E_SHAPE
+    # a 2^20 x 2^20 output in 256 x 256 tiles -> 2^24 workgroups
+    assert L.fos_qlinear_fwd(f, f, f, f, f, f, 1 << 20, 1 << 20, 64, f, None) == fos.FOS_E_SHAPE
+    assert L.fos_mx_qlinear_fwd(f, f, f, f, 1 << 20, 1 << 20, 256, f, None) == fos.FOS_E_SHAPE
+    # MXFP4 quantize: 512 blocks of 32 per workgroup
+    assert L.fos_mx_quantize(f, 1 << 20, (1 << 18) + 32, f, f, None) == fos.FOS_E_SHAPE
+
+
 def test_quantize_null_config():
     assert q(None) == fos.FOS_E_NULL
 
