@@ -18,21 +18,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk_max_abs(uint32_t m, uint32_t w) {
-  u16x2 a = __builtin_bit_cast(u16x2, m);
-  u16x2 b = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
-}
-
-__device__ __forceinline__ uint32_t pk_max_abs4(uint32_t m, const uint4& w) {
-  m = pk_max_abs(m, w.x);
-  m = pk_max_abs(m, w.y);
-  m = pk_max_abs(m, w.z);
-  return pk_max_abs(m, w.w);
-}
-
 // Block-wide max of `bits` (fp32 patterns of non-negative values) -> partials[block].
 __device__ __forceinline__ void write_partial(uint32_t bits, float* partials) {
   bits = block_max_u32(bits);
@@ -58,8 +43,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const uint4* __rest
     for (int u = 0; u < kUnroll; ++u) m = pk_max_abs4(m, w[u]);
   }
   for (; i < n16; i += stride) m = pk_max_abs4(m, x[i]);
-  const uint32_t bits = max(m & 0xffffu, m >> 16) << 16;
-  write_partial(bits, partials);
+  write_partial(pk_max_to_f32_bits(m), partials);
 }
 
 // Hadamard along rows: every 16-value block (two 16-byte chunks) is transformed.

@@ -45,6 +45,25 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   return m;
 }
 
+// Running max of |bf16| over packed pairs: integer max of each 16-bit half with the
+// sign cleared (for non-negative floats the bit order is the value order).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_abs(uint32_t m, uint32_t w) {
+  u16x2 a = __builtin_bit_cast(u16x2, m);
+  u16x2 b = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+__device__ __forceinline__ uint32_t pk_max_abs4(uint32_t m, const uint4& w) {
+  m = pk_max_abs(m, w.x);
+  m = pk_max_abs(m, w.y);
+  m = pk_max_abs(m, w.z);
+  return pk_max_abs(m, w.w);
+}
+// fp32 bit pattern of the larger of the two packed bf16 magnitudes.
+__device__ __forceinline__ uint32_t pk_max_to_f32_bits(uint32_t m) {
+  return max(m & 0xffffu, m >> 16) << 16;
+}
+
 // Maximum of the n non-negative partial maxima written by the tensor-scale pass
 // (n a multiple of 4, n <= 1024 = 4 * 256; `p` 16-byte aligned), by a workgroup of
 // 256 threads: one 16-byte load per thread, then the workgroup max.
@@ -283,6 +302,19 @@ __device__ __forceinline__ void cand_codes_sr(const float (&x)[16], float d, flo
   c.lo = lo;
   c.hi = hi;
   c.err = err;
+}
+
+// Store one block's nibbles and scale byte with non-temporal stores, for kernels whose
+// workgroups write whole runs of consecutive blocks (the row-wise kernels): the
+// outputs are written once and not read back, and keeping them out of the caches
+// measurably shortens the quantize step.  Kernels that write scattered pieces of
+// lines (tile, 2D) keep cached stores, which let L2 merge the pieces.
+__device__ __forceinline__ void store_block_stream(uint8_t* data, uint8_t* scales,
+                                                   int64_t data_off, int64_t scale_off,
+                                                   const Cand& c) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(v2u{c.lo, c.hi}, reinterpret_cast<v2u*>(data + data_off));
+  __builtin_nontemporal_store((uint8_t)c.s, scales + scale_off);
 }
 
 // Per-lane 16-value block amax (a chain of 3-input maxima with |.| modifiers).

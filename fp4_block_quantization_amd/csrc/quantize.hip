@@ -60,18 +60,8 @@ __device__ __forceinline__ void store_block(uint8_t* data, uint8_t* scales, int6
   scales[scale_off] = (uint8_t)c.s;
 }
 
-// The same with non-temporal stores, for kernels whose workgroups write whole runs of
-// consecutive blocks (the row-wise kernel): the outputs are written once and not read
-// back, and keeping them out of the caches measurably shortens the quantize step.
-// Kernels that write scattered pieces of lines (tile, 2D) keep the cached stores,
-// which let L2 merge the pieces.
-__device__ __forceinline__ void store_block_stream(uint8_t* data, uint8_t* scales,
-                                                   int64_t data_off, int64_t scale_off,
-                                                   const Cand& c) {
-  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(v2u{c.lo, c.hi}, reinterpret_cast<v2u*>(data + data_off));
-  __builtin_nontemporal_store((uint8_t)c.s, scales + scale_off);
-}
+// (Row-wise kernels, whose workgroups write whole runs of consecutive blocks, use
+// store_block_stream instead.)
 
 // ------------------------------------------------------------------ row-wise, 1D
 // Each lane owns blocks b and b + 256 of its workgroup's 512; both blocks' four

@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "fos_quantize_scaled": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
         "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
+        "fos_dequantize_hadamard": ([P, P, P, I64, I64, ctypes.c_uint64, ctypes.c_int, P, P],
+                                    ctypes.c_int),
         "fos_qlinear_fwd": ([P, P, P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
         "fos_qlinear_bwd": ([P] * 12 + [I64, I64, I64, P, P, P], ctypes.c_int),
         "fos_mx_quantize": ([P, I64, I64, P, P, P], ctypes.c_int),
