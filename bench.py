@@ -6,13 +6,16 @@ A step is one fos_quantize call (tensor-scale pass + fused 4/6 quantize kernel) 
 weight workload 4096x12288 bf16 (1D 16-value row blocks, 4/6, round-to-nearest-even),
 the configuration the headline metric is quoted on.  Inputs are resident in HBM
 before timing; three input/output sets (> 256 MB of inputs) rotate so that no call
-finds its input in the 256 MB Infinity Cache.  Times come from HIP events on the
+finds its input in the 256 MB Infinity Cache.  Before the first timed loop the step
+runs back to back for half a second (untimed) so that the GPU is at its steady
+clock; then W warm-up steps and K timed steps.  Times come from HIP events on the
 stream the kernels are launched on (torch's current stream).
 
 Printed: ONE JSON line with the headline (quantize GB/s of algorithmic bytes), the
 roofline of the dominant kernel (the quantize kernel timed alone, given the tensor
 scale), the CPU oracle timed on a bounded sample, and the other hot-path rows
-(column-wise, Hadamard + stochastic rounding, 2D, dequantize, qlinear TFLOP/s).
+(column-wise, Hadamard + stochastic rounding, 2D, dequantize, qlinear TFLOP/s from
+quantized and from bf16 activations, backward, MXFP4).
 """
 from __future__ import annotations
 
@@ -48,6 +51,21 @@ def source_hash() -> str:
 def quant_bytes(rows, cols, n_out=1):
     n = rows * cols
     return 2 * n + n_out * (n // 2 + n // 16) + 4
+
+
+def settle(fn, rotate, seconds):
+    """Run fn(i) back to back for `seconds` of wall time, untimed.  An idle GPU starts
+    at a low clock and takes tens of milliseconds of sustained work to reach its
+    steady one; without this the first timed loop of a fresh process can read
+    half the steady rate."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn(i % rotate)
+            i += 1
+        torch.cuda.synchronize()
 
 
 def time_loop(fn, steps, warmup, rotate):
@@ -123,10 +141,12 @@ class QuantCase:
         self.bad |= self._ts(*self.args_ts[i])
 
 
-def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1):
+def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.0):
     R, C = x_cpu.shape
     sets = min(8, max(3, -(-300 * 2 ** 20 // (2 * R * C))))   # > 256 MB of inputs rotate
     case = QuantCase(fos, x_cpu, cfg_kw, sets)
+    if settle_s > 0:
+        settle(case.step, sets, settle_s)
     ms = time_loop(case.step, steps, warmup, sets)
     ms_k = time_loop(case.scaled, steps, warmup, sets)
     ms_a = time_loop(case.scale_only, steps, warmup, sets)
@@ -220,6 +240,41 @@ def bench_qlinear(fos, x_cpu, w_cpu, steps, warmup):
     flops = 2 * M * N * K
     return {"shape": [M, N, K], "flop": flops, "ms": ms, "TFLOPs": flops / ms / 1e9,
             "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+
+
+def bench_qlinear_act(fos, x_cpu, w_cpu, steps, warmup):
+    """The c5 layer from a bf16 activation (fos_qlinear_fwd_act): X's quantization and
+    the GEMM in one call, with X's tensor scale computed in the call (two passes over
+    X) or given (one pass)."""
+    import ctypes
+    import torch
+    dev = "cuda:0"
+    lib = fos.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    x = x_cpu.to(dev)
+    wq = fos.quantize(w_cpu.to(dev))
+    M, K = x.shape
+    N = wq.shape[0]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws = fos.qlinear_act_workspace(M, K, dev)
+    t = torch.zeros(1, dtype=torch.float32, device=dev)
+    cfg = fos.make_config()
+    f = lib.fos_qlinear_fwd_act
+    flops = 2 * M * N * K
+    out = {"shape": [M, N, K], "flop": flops}
+    for name, given in (("scale_computed", 0), ("scale_given", 1)):
+        args = (ctypes.byref(cfg), _vp(x), _vp(t), given, _vp(wq.data), _vp(wq.scales),
+                _vp(wq.tensor_scale), M, N, K, _vp(y), _vp(ws), ws.numel(), stream)
+        bad = [0]
+
+        def fn(i):
+            bad[0] |= f(*args)
+        ms = time_loop(fn, max(10, steps // 2), max(15, warmup), 1)
+        if bad[0]:
+            raise RuntimeError("fos_qlinear_fwd_act returned an error status")
+        out[name] = {"ms": ms, "TFLOPs": flops / ms / 1e9,
+                     "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+    return out
 
 
 def bench_qlinear_bwd(fos, x_cpu, w_cpu, dy_cpu, steps, warmup):
@@ -394,7 +449,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one piece (c2_step, c2_kernel, c3_kernel, c4a_kernel, "
-                         "c4b_kernel, c5_qlinear, c5_mx_gemm, copy) and exit")
+                         "c4b_kernel, c5_qlinear, c5_qlinear_act, c5_qlinear_act_given, "
+                         "c5_mx_gemm, copy) and exit")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -441,6 +497,16 @@ def main():
             torch.cuda.synchronize()
             log(f"ran c5_mx_gemm x{args.steps}")
             return
+        if args.only in ("c5_qlinear_act", "c5_qlinear_act_given"):
+            wq = fos.quantize(W.make("c5_w").to("cuda:0"))
+            x = W.make("c5_x").to("cuda:0")
+            t = fos.tensor_scale(x) if args.only.endswith("given") else None
+            y = fos.qlinear_fwd_act(x, wq, x_tensor_scale=t)
+            for _ in range(args.steps):
+                fos.qlinear_fwd_act(x, wq, x_tensor_scale=t, out=y)
+            torch.cuda.synchronize()
+            log(f"ran {args.only} x{args.steps}")
+            return
         if args.only == "copy":
             a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
             b = torch.empty_like(a)
@@ -466,7 +532,8 @@ def main():
         return
 
     log("C2 weight quantize ...")
-    head = bench_quant(fos, "c2 weight 4096x12288, 1D rows, 4/6, RNE", x2, {}, args.steps, args.warmup)
+    head = bench_quant(fos, "c2 weight 4096x12288, 1D rows, 4/6, RNE", x2, {}, args.steps, args.warmup,
+                       settle_s=0.5)
     rows = {"c2_quantize": head}
     log(json.dumps(head))
     log("C2 dequantize ...")
@@ -493,6 +560,10 @@ def main():
     log("C5 qlinear ...")
     rows["c5_qlinear"] = bench_qlinear(fos, W.make("c5_x"), W.make("c5_w"), args.steps, args.warmup)
     log(json.dumps(rows["c5_qlinear"]))
+    log("C5 qlinear from bf16 X ...")
+    rows["c5_qlinear_act"] = bench_qlinear_act(fos, W.make("c5_x"), W.make("c5_w"), args.steps,
+                                               args.warmup)
+    log(json.dumps(rows["c5_qlinear_act"]))
     log("C5 qlinear backward ...")
     rows["c5_qlinear_bwd"] = bench_qlinear_bwd(fos, W.make("c5_x"), W.make("c5_w"),
                                                W.make("c5_dy"), args.steps, args.warmup)

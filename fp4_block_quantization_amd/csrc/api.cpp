@@ -150,6 +150,22 @@ fos_status launch_gemm(const uint8_t* a_data, const uint8_t* a_scales, const flo
              : FOS_E_HIP;
 }
 
+// Workspace of fos_qlinear_fwd_act: X's record, then the scale pass's scratch.
+struct ActLayout {
+  size_t scales, scratch, total;
+};
+bool act_layout(int64_t M, int64_t K, ActLayout& L) {
+  if (M < 0 || K < 0 || M >= kMaxDim || K >= kMaxDim) return false;
+  const uint64_t n = (uint64_t)M * (uint64_t)K;   // < 2^62
+  const auto up = [](uint64_t v) { return (v + 255) & ~(uint64_t)255; };
+  const uint64_t sc = up(n / 2), scr = up(sc + n / 16), tot = scr + kWorkspaceBytes;
+  if (tot > (uint64_t)SIZE_MAX) return false;
+  L.scales = (size_t)sc;
+  L.scratch = (size_t)scr;
+  L.total = (size_t)tot;
+  return true;
+}
+
 fos_status check_dequantize(const uint8_t* data, const uint8_t* scales, const float* tensor_scale,
                             int64_t rows, int64_t cols, int out_dtype, const void* out) {
   if (out_dtype != FOS_OUT_F32 && out_dtype != FOS_OUT_BF16) return FOS_E_FLAGS;
@@ -273,6 +289,51 @@ fos_status fos_qlinear_fwd(const uint8_t* x_data, const uint8_t* x_scales,
   if (st != FOS_OK) return st;
   return launch_gemm(x_data, x_scales, x_tensor_scale, w_data, w_scales, w_tensor_scale, M, N, K,
                      y_bf16, stream);
+}
+
+size_t fos_qlinear_act_workspace_bytes(int64_t M, int64_t K) {
+  ActLayout L;
+  return act_layout(M, K, L) ? L.total : 0;
+}
+
+fos_status fos_qlinear_fwd_act(const fos_quant_config* cfg, const void* x_bf16,
+                               float* x_tensor_scale, int x_scale_given,
+                               const uint8_t* w_data, const uint8_t* w_scales,
+                               const float* w_tensor_scale, int64_t M, int64_t N, int64_t K,
+                               void* y_bf16, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  fos_status st = check_config(cfg);
+  if (st != FOS_OK) return st;
+  if (cfg->outputs != FOS_OUT_ROWWISE) return FOS_E_FLAGS;
+  if ((st = check_input(cfg, x_bf16, M, K)) != FOS_OK) return st;
+  ActLayout L;
+  if (!act_layout(M, K, L)) return FOS_E_SHAPE;
+  if (!x_tensor_scale) return FOS_E_NULL;
+  if (!aligned(x_tensor_scale, 4)) return FOS_E_ALIGN;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return FOS_E_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xd = ws;
+  uint8_t* xs = ws + L.scales;
+  void* scratch = ws + L.scratch;
+  if ((st = check_gemm(xd, xs, x_tensor_scale, w_data, w_scales, w_tensor_scale, M, N, K,
+                       y_bf16)) != FOS_OK)
+    return st;
+  fos::QuantArgs a = make_args(cfg, x_bf16, M, K, x_scale_given ? x_tensor_scale : nullptr, xd,
+                               xs, nullptr, nullptr);
+  if (fos::quantize_grid(a) > fos::kMaxGrid) return FOS_E_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!x_scale_given) {
+    int npartials = 0;
+    if ((st = launch_scale(cfg, x_bf16, M, K, x_tensor_scale, scratch, false, &npartials, s)) !=
+        FOS_OK)
+      return st;
+    a.partials = static_cast<const float*>(scratch);
+    a.npartials = npartials;
+    a.tscale_out = x_tensor_scale;
+  }
+  if (fos::launch_quantize(a, s) != hipSuccess) return FOS_E_HIP;
+  return launch_gemm(xd, xs, x_tensor_scale, w_data, w_scales, w_tensor_scale, M, N, K, y_bf16,
+                     stream);
 }
 
 fos_status fos_qlinear_bwd(const uint8_t* dy_data, const uint8_t* dy_scales,

@@ -59,6 +59,9 @@ def _load() -> ctypes.CDLL:
                                     ctypes.c_int),
         "fos_qlinear_fwd": ([P, P, P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
         "fos_qlinear_bwd": ([P] * 12 + [I64, I64, I64, P, P, P], ctypes.c_int),
+        "fos_qlinear_act_workspace_bytes": ([I64, I64], SZ),
+        "fos_qlinear_fwd_act": ([cfgp, P, P, ctypes.c_int, P, P, P, I64, I64, I64, P, P, SZ, P],
+                                ctypes.c_int),
         "fos_mx_quantize": ([P, I64, I64, P, P, P], ctypes.c_int),
         "fos_mx_dequantize": ([P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_mx_qlinear_fwd": ([P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
@@ -186,6 +189,16 @@ def fos_qlinear_bwd(dy, dyt, xt, wt, M: int, N: int, K: int, dx: Optional[torch.
                                 _ptr(dw), _stream(dev)), "fos_qlinear_bwd")
 
 
+def fos_qlinear_fwd_act(cfg: FosQuantConfig, x: torch.Tensor, x_t: torch.Tensor,
+                        x_scale_given: bool, w_data, w_scales, w_t, N: int, y: torch.Tensor,
+                        ws: torch.Tensor) -> None:
+    M, K = x.shape
+    _check(_lib.fos_qlinear_fwd_act(ctypes.byref(cfg), _ptr(x), _ptr(x_t), int(bool(x_scale_given)),
+                                    _ptr(w_data), _ptr(w_scales), _ptr(w_t), M, N, K, _ptr(y),
+                                    _ptr(ws), ws.numel(), _stream(x.device)),
+           "fos_qlinear_fwd_act")
+
+
 # ---------------------------------------------------------------- tensor-level API
 
 @dataclass
@@ -302,6 +315,55 @@ def qlinear_fwd(xq: NVFP4Tensor, wq: NVFP4Tensor, out: Optional[torch.Tensor] = 
         raise ValueError("out must be a contiguous bf16 [M, N] tensor")
     fos_qlinear_fwd(xq.data, xq.scales, xq.tensor_scale, wq.data, wq.scales, wq.tensor_scale,
                     M, N, K, y)
+    return y
+
+
+def qlinear_act_workspace(M: int, K: int, device) -> torch.Tensor:
+    """A workspace for qlinear_fwd_act on X [M, K] (torch allocations are 256-byte
+    aligned)."""
+    n = int(_lib.fos_qlinear_act_workspace_bytes(M, K))
+    if n == 0:
+        raise ValueError("unsupported activation shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def act_record(ws: torch.Tensor, M: int, K: int, tensor_scale: torch.Tensor,
+               block: str = "1d", hadamard_seed: Optional[int] = None) -> NVFP4Tensor:
+    """Views of the record of X that qlinear_fwd_act leaves in its workspace."""
+    up = lambda v: (v + 255) // 256 * 256
+    nd, ns = M * K // 2, M * K // 16
+    data = ws[:nd].view(M, K // 2)
+    scales = ws[up(nd):up(nd) + ns].view(M, K // 16)
+    return NVFP4Tensor(data, scales, tensor_scale, "row", block, hadamard_seed)
+
+
+def qlinear_fwd_act(x: torch.Tensor, wq: NVFP4Tensor, rule: str = "4/6", rounding: str = "rne",
+                    block: str = "1d", hadamard_seed: Optional[int] = None,
+                    sr_seed: Optional[int] = None, x_tensor_scale: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, return_record: bool = False):
+    """Y = deq(Q(X)) deq(Wq)^T in bf16 from a bf16 activation X [M, K] and a weight
+    record Wq [N, K]: X is quantized with the given options inside the call.  With
+    ``x_tensor_scale`` (device fp32 [1], e.g. a delayed scale) X is read once;
+    otherwise its tensor scale is computed.  ``return_record`` also returns X's
+    record (views of a fresh workspace)."""
+    _check_input(x)
+    _check_record(wq)
+    M, K = x.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if wq.data.device != x.device:
+        raise ValueError("x and the weight record are on different devices")
+    cfg = make_config(rule, rounding, block, ("row",), hadamard_seed, sr_seed)
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    if y.shape != (M, N) or y.dtype != torch.bfloat16 or not y.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    given = x_tensor_scale is not None
+    t = x_tensor_scale if given else torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = qlinear_act_workspace(M, K, x.device)
+    fos_qlinear_fwd_act(cfg, x, t, given, wq.data, wq.scales, wq.tensor_scale, N, y, ws)
+    if return_record:
+        return y, act_record(ws, M, K, t, block, hadamard_seed)
     return y
 
 

@@ -58,7 +58,9 @@ typedef enum {
   FOS_E_FLAGS = 4,     /* unknown enum value, wrong struct_size, or an unsupported
                           option combination (e.g. Hadamard with 2D blocks)         */
   FOS_E_WORKSPACE = 5, /* workspace NULL, not 16-byte aligned, or smaller than
-                          fos_workspace_bytes()                                     */
+                          fos_workspace_bytes() (fos_qlinear_fwd_act: not 256-byte
+                          aligned, or smaller than
+                          fos_qlinear_act_workspace_bytes(M, K))                   */
   FOS_E_HIP = 6        /* a HIP launch failed                                        */
 } fos_status;
 
@@ -212,6 +214,45 @@ fos_status fos_qlinear_bwd(const uint8_t* dy_data, const uint8_t* dy_scales,
                            const uint8_t* wt_scales, const float* wt_tensor_scale,
                            int64_t M, int64_t N, int64_t K, void* dx_bf16, void* dw_bf16,
                            void* stream);
+
+/* Workspace bytes that fos_qlinear_fwd_act needs for an activation X [M][K]; 0 when
+ * M or K is negative or the size does not fit in size_t.  Layout of the workspace
+ * after a call (offsets from its start; P = round_up(M*K/2, 256),
+ * Q = round_up(P + M*K/16, 256)):
+ *   [0, M*K/2)                 nibbles of X's row-wise record  [M][K/2]
+ *   [P, P + M*K/16)            its E4M3 block scales           [M][K/16]
+ *   [Q, Q + fos_workspace_bytes())  scratch of the tensor-scale pass */
+size_t fos_qlinear_act_workspace_bytes(int64_t M, int64_t K);
+
+/* Quantized linear forward from a bf16 activation: the inference path of a linear
+ * layer whose weight was quantized ahead of time (Four Over Six documentation page,
+ * "Four Over Six": the quantized layer is simulated with a higher-precision matmul
+ * of the dequantized operands).  X [M][K] is quantized with cfg into the workspace
+ * (its row-wise record, blocked along K), then multiplied with Wq as in
+ * fos_qlinear_fwd, on the same stream:
+ *   Y = fos_qlinear_fwd(record of X, Wq)
+ * with results identical to fos_quantize (or fos_quantize_scaled) followed by
+ * fos_qlinear_fwd.  The record stays in the workspace (layout above) until the
+ * workspace is reused.
+ *   x_tensor_scale: device fp32.  x_scale_given == 0: the call runs the tensor-scale
+ *     pass and writes t_x there.  x_scale_given != 0: the call reads a t_x that the
+ *     caller computed beforehand (delayed scaling, or fos_tensor_scale issued ahead
+ *     of time, e.g. on a second stream while the previous layer runs), and X is
+ *     read once.
+ *   cfg: outputs must be FOS_OUT_ROWWISE.  Any rule and rounding; 2D blocks need
+ *     M % 16 == 0; with the Hadamard transform W must carry the same transform
+ *     along K, so that it cancels in the product.
+ *   x_bf16 [M][K] 16-byte aligned; workspace 256-byte aligned, at least
+ *     fos_qlinear_act_workspace_bytes(M, K) bytes; Wq, y_bf16, M, N, K as for
+ *     fos_qlinear_fwd (K % 64 == 0).
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_WORKSPACE,
+ * FOS_E_HIP. */
+fos_status fos_qlinear_fwd_act(const fos_quant_config* cfg, const void* x_bf16,
+                               float* x_tensor_scale, int x_scale_given,
+                               const uint8_t* w_data, const uint8_t* w_scales,
+                               const float* w_tensor_scale, int64_t M, int64_t N, int64_t K,
+                               void* y_bf16, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* ---- MXFP4 -------------------------------------------------------------------
  * Ultralytics glossary "FP4", "How FP4 works": MXFP4 (OCP Microscaling) groups 32

@@ -151,6 +151,38 @@ def test_qlinear_validation():
     assert L.fos_qlinear_fwd(f, f, f, f, f, f, 1 << 20, 256, 1 << 13, f, None) == fos.FOS_E_SHAPE
 
 
+def test_qlinear_act_validation():
+    """fos_qlinear_fwd_act checks the quantize options, the activation, the workspace
+    and the GEMM operands before any launch."""
+    L = fos.lib()
+    f, z = FAKE, None
+    M, N, K = 256, 256, 256
+    need = L.fos_qlinear_act_workspace_bytes(M, K)
+    assert need == M * K // 2 + M * K // 16 + L.fos_workspace_bytes()
+    assert L.fos_qlinear_act_workspace_bytes(-1, 64) == 0
+    big = ctypes.c_void_p(0x1000000)                        # 256-byte aligned
+
+    def call(c=None, x=f, t=f, given=0, wd=f, wsc=f, wt=f, m=M, n=N, k=K, y=f, ws=big, wsb=need):
+        c = cfg() if c is None else c
+        return L.fos_qlinear_fwd_act(ctypes.byref(c), x, t, given, wd, wsc, wt, m, n, k, y, ws, wsb,
+                                     None)
+    assert call(c=cfg(outputs=("col",))) == fos.FOS_E_FLAGS
+    assert call(c=cfg(outputs=("row", "col"))) == fos.FOS_E_FLAGS
+    assert call(k=100) == fos.FOS_E_SHAPE                   # K % 16
+    assert call(k=80) == fos.FOS_E_SHAPE                    # K % 64 (GEMM)
+    assert call(m=0) == fos.FOS_E_SHAPE
+    assert call(c=cfg(block="2d"), m=24) == fos.FOS_E_SHAPE
+    assert call(x=z) == fos.FOS_E_NULL
+    assert call(x=MIS) == fos.FOS_E_ALIGN
+    assert call(t=z) == fos.FOS_E_NULL
+    assert call(ws=z) == fos.FOS_E_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x1000010)) == fos.FOS_E_WORKSPACE   # 16- but not 256-aligned
+    assert call(wsb=need - 1) == fos.FOS_E_WORKSPACE
+    assert call(wd=z) == fos.FOS_E_NULL
+    assert call(y=z) == fos.FOS_E_NULL
+    assert call(wd=MIS) == fos.FOS_E_ALIGN
+
+
 def test_qlinear_bwd_validation():
     """All arguments are checked before either product launches; a skipped product's
     operands may be NULL."""
