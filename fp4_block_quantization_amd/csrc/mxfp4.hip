@@ -167,21 +167,24 @@ struct MxOperands {
 };
 
 // This wave's share of one stage: 64 rows of each operand, 8 + 8 data copies (8 rows
-// of 128 bytes each) and 2 + 2 scale copies (32 rows of 8 bytes each).
-__device__ __forceinline__ void mx_stage_load(MxStage& st, const MxOperands& p, int sc, int wave) {
+// of 128 bytes each) and 2 + 2 scale copies (32 rows of 8 bytes each), issued as two
+// halves of 10 copies (half j: data row-groups 4j..4j+3 and scale row-group j).
+__device__ __forceinline__ void mx_stage_load_half(MxStage& st, const MxOperands& p, int sc,
+                                                   int wave, int j) {
   const int od = sc * kMxRowBytes, os = sc * kMxRowScales;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 4 * j; q < 4 * j + 4; ++q) {
     const int so = od + q * (int)p.group_stride;
     dma16(p.a, st.a + (64 * wave + 8 * q) * kMxRowBytes, p.oa[q & 1], so);
     dma16(p.b, st.b + (64 * wave + 8 * q) * kMxRowBytes, p.ob[q & 1], so);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int so = os + j * (int)p.scale_stride;
-    dma4(p.sa, st.sa + (64 * wave + 32 * j) * kMxRowScales, p.osa, so);
-    dma4(p.sb, st.sb + (64 * wave + 32 * j) * kMxRowScales, p.osb, so);
-  }
+  const int so = os + j * (int)p.scale_stride;
+  dma4(p.sa, st.sa + (64 * wave + 32 * j) * kMxRowScales, p.osa, so);
+  dma4(p.sb, st.sb + (64 * wave + 32 * j) * kMxRowScales, p.osb, so);
+}
+__device__ __forceinline__ void mx_stage_load(MxStage& st, const MxOperands& p, int sc, int wave) {
+  mx_stage_load_half(st, p, sc, wave, 0);
+  mx_stage_load_half(st, p, sc, wave, 1);
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -192,14 +195,22 @@ __device__ __forceinline__ i32x8 mx_operand(const uint8_t* base, int row, int g)
   return i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 }
 
-// Multiply the four 64-wide k-steps of a stage.  In k-step s, lane (lr, h) supplies
-// row lr's 32 values of k block 2s + h (granule 2s + h) and that block's E8M0 scale
-// (byte 2s + h of the row's 8).  The next k-step's granules are read from LDS while
-// the current k-step's 16 MFMAs issue.
+// Multiply the four 64-wide k-steps of a stage, and (kLoad) copy stage `next_sc` of
+// the operands into `next` meanwhile.  In k-step s, lane (lr, h) supplies row lr's 32
+// values of k block 2s + h (granule 2s + h) and that block's E8M0 scale (byte 2s + h
+// of the row's 8).  All scale bytes and the first k-step's operands are read up
+// front; each k-step's 8 operand reads for the next k-step are issued between its
+// first 8 MFMAs (scheduling groups: one MFMA, one LDS read), so that every read has
+// at least 8 MFMAs (about 256 cycles) to land.  The next stage's 20 copies go out in
+// k-steps 0 and 1, one after each of their first 10 MFMAs, leaving k-steps 2 and 3
+// for them to land.  (Issued in one burst, the copies hold up the wave's instruction
+// stream for hundreds of cycles while the matrix pipe idles; left to itself the
+// scheduler also reads each operand right before its first use and waits for it.)
 constexpr int NKS = kMxSuper / 64;
+template <bool kLoad>
 __device__ __forceinline__ void mx_stage_mma(const MxStage& st, f32x16 (&acc)[4][4], int ra,
-                                             int rb, int h) {
-  // keep the caller's copies of the next stage ahead of this stage's MFMAs
+                                             int rb, int h, MxStage& next, const MxOperands& p,
+                                             int next_sc, int wave) {
   __builtin_amdgcn_sched_barrier(0);
   uint2 sa[4], sb[4];
   i32x8 A[4], B[4];
@@ -210,9 +221,16 @@ __device__ __forceinline__ void mx_stage_mma(const MxStage& st, f32x16 (&acc)[4]
     A[i] = mx_operand(st.a, ra + 32 * i, h);
     B[i] = mx_operand(st.b, rb + 32 * i, h);
   }
+  __builtin_amdgcn_sched_barrier(0);
   const int sh = 8 * h;
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
+    int xa[4], xb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xa[i] = (int)(((s < 2) ? sa[i].x : sa[i].y) >> (16 * (s & 1) + sh));
+      xb[i] = (int)(((s < 2) ? sb[i].x : sb[i].y) >> (16 * (s & 1) + sh));
+    }
     i32x8 An[4], Bn[4];
     if (s + 1 < NKS) {
 #pragma unroll
@@ -221,18 +239,36 @@ __device__ __forceinline__ void mx_stage_mma(const MxStage& st, f32x16 (&acc)[4]
         Bn[i] = mx_operand(st.b, rb + 32 * i, 2 * (s + 1) + h);
       }
     }
-    int xa[4], xb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xa[i] = (int)(((s < 2) ? sa[i].x : sa[i].y) >> (16 * (s & 1) + sh));
-      xb[i] = (int)(((s < 2) ? sb[i].x : sb[i].y) >> (16 * (s & 1) + sh));
-    }
+    const bool copies = kLoad && s < 2;
+    if (copies) mx_stage_load_half(next, p, next_sc, wave, s);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int n = 0; n < 4; ++n)
         acc[i][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[n], acc[i][n], 4, 4,
                                                                      0, xa[i], 0, xb[n]);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);       // the 8 scale shifts
+    if (s + 1 < NKS) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        if (copies) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one copy
+      }
+      if (copies) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < NKS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -242,7 +278,7 @@ __device__ __forceinline__ void mx_stage_mma(const MxStage& st, f32x16 (&acc)[4]
     }
   }
   // MFMAs touch no memory, so without this the scheduler may sink them below the
-  // next workgroup barrier, leaving the next stage's copies nothing to hide behind
+  // next workgroup barrier
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -298,18 +334,16 @@ void mx_gemm_kernel(const uint8_t* __restrict__ ad, const uint8_t* __restrict__ 
   for (; sc + 1 < nsc; sc += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    mx_stage_load(st1, p, sc + 1, wave);
-    mx_stage_mma(st0, acc, ra, rb, h);
+    mx_stage_mma<true>(st0, acc, ra, rb, h, st1, p, sc + 1, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // unconditional (a redundant copy of the last stage when none is left): a branch
     // here lets the compiler sink the previous stage's MFMAs past the barrier
-    mx_stage_load(st0, p, min(sc + 2, nsc - 1), wave);
-    mx_stage_mma(st1, acc, ra, rb, h);
+    mx_stage_mma<true>(st1, acc, ra, rb, h, st0, p, min(sc + 2, nsc - 1), wave);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (sc < nsc) mx_stage_mma(st0, acc, ra, rb, h);
+  if (sc < nsc) mx_stage_mma<false>(st0, acc, ra, rb, h, st1, p, 0, wave);
   store_tile(y, M, N, tm, tn, wave, lr, h, 1.0f, acc);
 }
 

@@ -260,20 +260,27 @@ struct LdsOperands {
   uint32_t group_stride;      // bytes between row-groups (8 rows)
 };
 
-// Issue this wave's share of one super-chunk: 8 + 8 data instructions and 1 + 1
-// scale instructions (64 rows of each operand per wave).  Row-group q of the wave
-// starts 8*q rows further on; the granule swizzle only depends on q's parity, so the
-// per-lane offset is one of two values and the rest is a scalar offset.
-__device__ __forceinline__ void stage_load(LdsStage& st, const LdsOperands& p, int sc, int wave) {
-  const int od = sc * kRowBytes, os = sc * kRowScales;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int so = od + q * (int)p.group_stride;
-    dma16(p.a, st.a + (64 * wave + 8 * q) * kRowBytes, p.oa[q & 1], so);
-    dma16(p.b, st.b + (64 * wave + 8 * q) * kRowBytes, p.ob[q & 1], so);
+// This wave's share of one super-chunk: 8 + 8 data instructions and 1 + 1 scale
+// instructions (64 rows of each operand per wave).  Row-group q of the wave starts
+// 8*q rows further on; the granule swizzle only depends on q's parity, so the
+// per-lane offset is one of two values and the rest is a scalar offset.  Part j < 8
+// copies row-group j of both operands, part 8 both scale blocks.
+__device__ __forceinline__ void stage_load_part(LdsStage& st, const LdsOperands& p, int sc,
+                                                int wave, int j) {
+  if (j < 8) {
+    const int so = sc * kRowBytes + j * (int)p.group_stride;
+    dma16(p.a, st.a + (64 * wave + 8 * j) * kRowBytes, p.oa[j & 1], so);
+    dma16(p.b, st.b + (64 * wave + 8 * j) * kRowBytes, p.ob[j & 1], so);
+  } else {
+    const int os = sc * kRowScales;
+    dma16(p.sa, st.sa + 64 * wave * kRowScales, p.osa, os);
+    dma16(p.sb, st.sb + 64 * wave * kRowScales, p.osb, os);
   }
-  dma16(p.sa, st.sa + 64 * wave * kRowScales, p.osa, os);
-  dma16(p.sb, st.sb + 64 * wave * kRowScales, p.osb, os);
+}
+constexpr int kLoadParts = 9;
+__device__ __forceinline__ void stage_load(LdsStage& st, const LdsOperands& p, int sc, int wave) {
+#pragma unroll
+  for (int j = 0; j < kLoadParts; ++j) stage_load_part(st, p, sc, wave, j);
 }
 
 template <bool kHi>
@@ -302,8 +309,14 @@ __device__ __forceinline__ void group_scales(const uint2 (&sc)[4], int gq, h2 (&
 // the 16 MFMAs of k-step s issue (one MFMA, then up to five VALU instructions,
 // repeated), so the conversion runs in the MFMA pipe's shadow instead of in front of
 // it; the next group's granules are read from LDS three k-steps before they are used.
+// With kLoad, the copies of super-chunk `next_sc` into `next` go out two per k-step
+// in k-steps 0-8, right after the k-step's first MFMA, which leaves seven k-steps for
+// them to land.  (Issued in one burst, they hold up the wave's in-order instruction
+// stream while the matrix pipe idles.)
+template <bool kLoad>
 __device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4], int ra,
-                                               int rb, int h) {
+                                          int rb, int h, LdsStage& next, const LdsOperands& p,
+                                          int next_sc, int wave) {
   uint2 sca[4], scb[4];
   uint4 ga[4], gb[4], na[4], nb[4];
 #pragma unroll
@@ -351,6 +364,8 @@ __device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4
         Bn[i] = dequant8(word(gb[i], jj1), db[i][jj1 >> 1]);
       }
     }
+    const bool copies = kLoad && s < kLoadParts;
+    if (copies) stage_load_part(next, p, next_sc, wave, s);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -360,6 +375,7 @@ __device__ __forceinline__ void stage_mma(const LdsStage& st, f32x16 (&acc)[4][4
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      if (copies && m == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // the copies
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -423,26 +439,24 @@ void qlinear_lds_kernel(const uint8_t* __restrict__ xd, const uint8_t* __restric
   const int rb = (wave & 1) * 128 + lr;      // and first B row
   const int nsc = K / kSuper;
   // Each step: wait for this wave's copies of the stage about to be used, barrier
-  // (so every wave's copies have landed and the other stage is no longer read), start
-  // copying the next super-chunk into the other stage, multiply.  A single-exit loop
-  // keeps the 256 accumulator registers in place.
+  // (so every wave's copies have landed and the other stage is no longer read), then
+  // multiply while copying the next super-chunk into the other stage.  A single-exit
+  // loop keeps the 256 accumulator registers in place.
   stage_load(st0, p, 0, wave);
   int sc = 0;
   for (; sc + 1 < nsc; sc += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    stage_load(st1, p, sc + 1, wave);
-    stage_mma(st0, acc, ra, rb, h);
+    stage_mma<true>(st0, acc, ra, rb, h, st1, p, sc + 1, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (sc + 2 < nsc) stage_load(st0, p, sc + 2, wave);
-    stage_mma(st1, acc, ra, rb, h);
+    // unconditional (a redundant copy of the last super-chunk when none is left): a
+    // branch here lets the compiler sink the previous stage's MFMAs past the barrier
+    stage_mma<true>(st1, acc, ra, rb, h, st0, p, min(sc + 2, nsc - 1), wave);
   }
-  if (sc < nsc) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    stage_mma(st0, acc, ra, rb, h);
-  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (sc < nsc) stage_mma<false>(st0, acc, ra, rb, h, st1, p, 0, wave);
 
   store_tile(y, M, N, tm, tn, wave, lr, h, xt[0] * wt[0], acc);
 }
