@@ -102,7 +102,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---- E4M3 (OCP "FN": bias 7, max 448) ------------------------------------------
-// Round r >= 0 (or +inf) to the nearest E4M3 value, ties to even, saturating to 448.
+// Round r >= 0 (or +inf) to the nearest E4M3 value, ties to even, saturating to 448:
+// the bit-level definition that fos_selftest_e4m3 holds the hardware conversion to.
 __device__ __forceinline__ uint32_t e4m3_encode(float r) {
   r = fminf(r, 448.0f);
   const uint32_t b = __float_as_uint(r);
@@ -234,11 +235,26 @@ __device__ __forceinline__ void build_scale_table(float2* tab, float t) {
   __syncthreads();
 }
 
-// Scale byte, decode scale and element reciprocal of a candidate (per block).
-__device__ __forceinline__ void cand_scale(float a, float u, const float2* tab, uint32_t& s,
-                                           float& d, float& inv) {
-  const float r = (a == 0.0f) ? 0.0f : a * u;
-  s = e4m3_encode(r);
+// E4M3 scale bytes of both candidates of a block: r_c = RN(a * u_c), clamped to 448
+// (0 when a == 0, also when u_c is infinite), converted by the hardware
+// (v_cvt_pk_fp8_f32: OCP E4M3, nearest-even, subnormals kept) -- one instruction for
+// the two candidates.  On [0, 448] the conversion returns e4m3_encode's code for
+// every fp32 value; fos_selftest_e4m3 checks that exhaustively on the device.
+__device__ __forceinline__ uint32_t e4m3_encode_pk_hw(float r0, float r1) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false) & 0xffffu;
+}
+__device__ __forceinline__ void cand_scale_bytes(float a, float u6, float u4, uint32_t& s6,
+                                                 uint32_t& s4) {
+  const bool zero = a == 0.0f;
+  const float r6 = zero ? 0.0f : fminf(a * u6, 448.0f);
+  const float r4 = zero ? 0.0f : fminf(a * u4, 448.0f);
+  const uint32_t w = e4m3_encode_pk_hw(r6, r4);
+  s6 = w & 0xffu;
+  s4 = w >> 8;
+}
+
+// Decode scale and element reciprocal of a candidate's scale byte.
+__device__ __forceinline__ void cand_lookup(uint32_t s, const float2* tab, float& d, float& inv) {
   const float2 e = tab[s];
   d = e.x;
   inv = e.y;
@@ -332,10 +348,11 @@ __device__ __forceinline__ Cand quantize_block(const float (&x)[16], const float
   const float a = amax16(x);
   Cand c6, c4;
   float inv6, inv4;
-  cand_scale(a, u6, tab, c6.s, c6.d, inv6);
+  cand_scale_bytes(a, u6, u4, c6.s, c4.s);
+  cand_lookup(c6.s, tab, c6.d, inv6);
   if (kSR) cand_codes_sr(x, c6.d, inv6, srq, c6); else cand_codes_rne(x, c6.d, inv6, c6);
   if (!kFourOverSix) return c6;
-  cand_scale(a, u4, tab, c4.s, c4.d, inv4);
+  cand_lookup(c4.s, tab, c4.d, inv4);
   if (kSR) cand_codes_sr(x, c4.d, inv4, srq, c4); else cand_codes_rne(x, c4.d, inv4, c4);
   return (c4.err < c6.err) ? c4 : c6;
 }

@@ -45,6 +45,11 @@ int64_t quantize_grid(const QuantArgs& a);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
+// Adds to *mismatches the number of disagreements between the hardware E4M3
+// conversion the quantize kernels use and the bit-level definition (e4m3_encode),
+// over every fp32 value in [0, 448].
+hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
                              int64_t rows, int64_t cols, bool bf16_out, void* out,
                              hipStream_t stream);

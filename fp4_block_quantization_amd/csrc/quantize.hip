@@ -259,12 +259,13 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
     const float am = row16_max(amax16(v));
     Cand c6, c4;
     float inv6, inv4;
-    cand_scale(am, tc.u6, tc.tab, c6.s, c6.d, inv6);
+    cand_scale_bytes(am, tc.u6, tc.u4, c6.s, c4.s);
+    cand_lookup(c6.s, tc.tab, c6.d, inv6);
     if (kSR) cand_codes_sr(v, c6.d, inv6, srq, c6); else cand_codes_rne(v, c6.d, inv6, c6);
     c6.err = row16_sum(c6.err);
     Cand c = c6;
     if (k46) {
-      cand_scale(am, tc.u4, tc.tab, c4.s, c4.d, inv4);
+      cand_lookup(c4.s, tc.tab, c4.d, inv4);
       if (kSR) cand_codes_sr(v, c4.d, inv4, srq, c4); else cand_codes_rne(v, c4.d, inv4, c4);
       c4.err = row16_sum(c4.err);
       if (c4.err < c6.err) c = c4;
@@ -319,6 +320,22 @@ hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Self-test of the hardware E4M3 conversion: every fp32 bit pattern in [0, 448] is
+// converted by e4m3_encode_pk_hw (both halves) and by e4m3_encode; each lane counts
+// its disagreements and adds a nonzero count to *mismatches.
+constexpr uint32_t kE4m3TestPatterns = 0x43E00001u;   // +0 .. 448.0 inclusive
+__global__ __launch_bounds__(kThreads) void selftest_e4m3_kernel(unsigned long long* mismatches) {
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t bad = 0;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < kE4m3TestPatterns; i += stride) {
+    const float r = __uint_as_float(i);
+    const uint32_t hw = e4m3_encode_pk_hw(r, r);
+    const uint32_t sw = e4m3_encode(r);
+    bad += ((hw & 0xffu) != sw) + ((hw >> 8) != sw);
+  }
+  if (bad) atomicAdd(mismatches, (unsigned long long)bad);
+}
+
 template <bool k46, bool kSR>
 hipError_t dispatch_rule(const QuantArgs& a, hipStream_t s) {
   if (a.two_d) return dispatch_2d<k46, kSR>(a, s);
@@ -340,6 +357,11 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.four_over_six)
     return a.sr ? dispatch_rule<true, true>(a, s) : dispatch_rule<true, false>(a, s);
   return a.sr ? dispatch_rule<false, true>(a, s) : dispatch_rule<false, false>(a, s);
+}
+
+hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t s) {
+  selftest_e4m3_kernel<<<4096, kThreads, 0, s>>>(mismatches);
+  return hipGetLastError();
 }
 
 }  // namespace fos

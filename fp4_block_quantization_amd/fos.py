@@ -54,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "fos_tensor_scale": ([cfgp, P, I64, I64, P, P, SZ, P], ctypes.c_int),
         "fos_quantize_scaled": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
         "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "fos_selftest_e4m3": ([P, P], ctypes.c_int),
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_dequantize_hadamard": ([P, P, P, I64, I64, ctypes.c_uint64, ctypes.c_int, P, P],
                                     ctypes.c_int),
@@ -154,6 +155,15 @@ def fos_quantize(cfg: FosQuantConfig, x: torch.Tensor, row_data, row_scales, col
                              _ptr(row_data), _ptr(row_scales), _ptr(col_data), _ptr(col_scales),
                              _ptr(tensor_scale), _ptr(ws), ws.numel(), _stream(x.device)),
            "fos_quantize")
+
+
+def selftest_e4m3(device="cuda:0") -> int:
+    """Number of fp32 values in [0, 448] whose hardware E4M3 conversion (used by the
+    quantize kernels for the block scales) differs from the bit-level rule; 0 on a
+    correct device."""
+    n = torch.zeros(1, dtype=torch.int64, device=device)
+    _check(_lib.fos_selftest_e4m3(_ptr(n), _stream(n.device)), "fos_selftest_e4m3")
+    return int(n.item())
 
 
 def fos_dequantize(data: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Tensor,

@@ -143,6 +143,16 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
                         uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Self-test of the hardware E4M3 conversion that the quantize kernels use for the
+ * block scales (gfx950's packed fp32 -> OCP E4M3 conversion, nearest-even): adds to
+ * *mismatches (device uint64, 8-byte aligned; the caller zeroes it) the number of
+ * fp32 values r in [0, 448] -- every bit pattern, 1,138,753,537 of them -- whose
+ * hardware code differs from the bit-level rule (E4M3 "FN" round-to-nearest-even,
+ * subnormals kept; Ultralytics glossary "FP4", "How FP4 works", for the E4M3 block
+ * scale).  A correct device gives 0.  Takes a few milliseconds.
+ * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_selftest_e4m3(unsigned long long* mismatches, void* stream);
+
 /* Dequantize one NVFP4 record: out[r][c] = RN_fp32(E2M1(q) * RN_fp32(E4M3(s) * t))
  * with the nibble's sign (-0 for code 8); FOS_OUT_BF16 rounds that fp32 value to
  * bf16 (nearest-even).  Works for row-wise, column-wise (giving X^T) and 2D records.

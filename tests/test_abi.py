@@ -151,6 +151,12 @@ def test_qlinear_validation():
     assert L.fos_qlinear_fwd(f, f, f, f, f, f, 1 << 20, 256, 1 << 13, f, None) == fos.FOS_E_SHAPE
 
 
+def test_selftest_validation():
+    L = fos.lib()
+    assert L.fos_selftest_e4m3(None, None) == fos.FOS_E_NULL
+    assert L.fos_selftest_e4m3(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
+
+
 def test_qlinear_act_validation():
     """fos_qlinear_fwd_act checks the quantize options, the activation, the workspace
     and the GEMM operands before any launch."""

@@ -103,6 +103,13 @@ def test_quantize_matches_oracle(fos, shape, cfg_name):
         assert_quant_equal(g, o)
 
 
+def test_hardware_e4m3_conversion_matches_rule(fos):
+    """The quantize kernels encode block scales with the hardware fp32 -> E4M3
+    conversion; on every fp32 value in [0, 448] it must give the bit-level rule's code
+    (nearest-even, subnormals kept) that the oracle implements."""
+    assert fos.selftest_e4m3() == 0
+
+
 @pytest.mark.parametrize("rows", [1, 3, 7])
 def test_row_wise_any_row_count(fos, rows):
     bits = bits_of(W.random_bf16(rows, 4096 + 48, 55 + rows, "student_t"))
