@@ -13,7 +13,9 @@ stream the kernels are launched on (torch's current stream).
 
 Printed: ONE JSON line with the headline (quantize GB/s of algorithmic bytes), the
 roofline of the dominant kernel (the quantize kernel timed alone, given the tensor
-scale), the CPU oracle timed on a bounded sample, and the other hot-path rows
+scale: its calls are captured in a HIP graph and replayed, so that the time per call
+is the GPU's and not the host's launch rate; the eager per-call time is reported
+beside it), the CPU oracle timed on a bounded sample, and the other hot-path rows
 (column-wise, Hadamard + stochastic rounding, 2D, dequantize, qlinear TFLOP/s from
 quantized and from bf16 activations, backward, MXFP4).
 """
@@ -84,6 +86,36 @@ def time_loop(fn, steps, warmup, rotate):
     return s.elapsed_time(e) / steps
 
 
+def graph_loop(make_fn, steps, warmup, rotate):
+    """Average ms per call of `steps` calls captured in one HIP graph (torch.cuda.CUDAGraph)
+    and replayed, so that the GPU runs the kernels back to back without waiting for the
+    host to launch each one.  make_fn(stream) returns fn(i) issuing call i on `stream`."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn = make_fn(side)
+        for i in range(max(3, warmup)):
+            fn(i % rotate)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn = make_fn(torch.cuda.current_stream())
+        for i in range(steps):
+            fn(i % rotate)
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) / steps
+
+
 def _vp(t):
     import ctypes
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
@@ -131,6 +163,17 @@ class QuantCase:
             self.args_ts.append((cref, x, R, C, t, _vp(self.ws), nws, stream))
         self.bad = 0
 
+    def on_stream(self, stream, scaled=True):
+        """fn(i) issuing call i (fos_quantize_scaled, or fos_quantize) on `stream`."""
+        import ctypes
+        h = ctypes.c_void_p(stream.cuda_stream)
+        args = [a[:-1] + (h,) for a in (self.args_qs if scaled else self.args_q)]
+        f = self._qs if scaled else self._q
+
+        def fn(i):
+            self.bad |= f(*args[i])
+        return fn
+
     def step(self, i):
         self.bad |= self._q(*self.args_q[i])
 
@@ -148,7 +191,8 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.0):
     if settle_s > 0:
         settle(case.step, sets, settle_s)
     ms = time_loop(case.step, steps, warmup, sets)
-    ms_k = time_loop(case.scaled, steps, warmup, sets)
+    ms_k_eager = time_loop(case.scaled, steps, warmup, sets)
+    ms_k = graph_loop(case.on_stream, steps, warmup, sets)
     ms_a = time_loop(case.scale_only, steps, warmup, sets)
     if case.bad:
         raise RuntimeError(f"{name}: a fos call returned an error status")
@@ -159,6 +203,7 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.0):
            "frac_step": b / ms / 1e6 / HBM_PEAK_GBS,
            "ms_quant_kernel": ms_k, "GBps_quant_kernel": b / ms_k / 1e6,
            "frac_quant_kernel": b / ms_k / 1e6 / HBM_PEAK_GBS,
+           "ms_quant_kernel_eager_calls": ms_k_eager,
            "ms_scale_kernel": ms_a, "GBps_scale_kernel": 2 * R * C / ms_a / 1e6}
     del case
     return row

@@ -103,6 +103,38 @@ def test_quantize_matches_oracle(fos, shape, cfg_name):
         assert_quant_equal(g, o)
 
 
+def test_graph_capture_replays_match_eager(fos):
+    """fos_quantize (scale pass + quantize) and fos_quantize_scaled captured in one HIP
+    graph: every replay, with eager work and synchronizations between the replays,
+    gives the bytes of the eager calls."""
+    x = W.random_bf16(272, 1040, 77, "student_t").to(DEV)
+    other = W.random_bf16(272, 1040, 78, "normal").to(DEV)
+    R, C = x.shape
+    ref = fos.quantize(x)
+    ref6 = fos.quantize(x, rule="6", tensor_scale=ref.tensor_scale)
+    torch.cuda.synchronize()
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    rd, rs = torch.empty(R, C // 2, **u8), torch.empty(R, C // 16, **u8)
+    rd6, rs6 = torch.empty(R, C // 2, **u8), torch.empty(R, C // 16, **u8)
+    t = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(int(fos.lib().fos_workspace_bytes()), **u8)
+    cfg, cfg6 = fos.make_config(), fos.make_config(rule="6")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fos.fos_quantize(cfg, x, rd, rs, None, None, t, ws)
+        fos.fos_quantize_scaled(cfg6, x, t, rd6, rs6)
+    for _ in range(3):
+        for buf in (rd, rs, rd6, rs6, t):
+            buf.zero_()
+        fos.quantize(other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(t, ref.tensor_scale)
+        assert torch.equal(rd, ref.data) and torch.equal(rs, ref.scales)
+        assert torch.equal(rd6, ref6.data) and torch.equal(rs6, ref6.scales)
+
+
 def test_hardware_e4m3_conversion_matches_rule(fos):
     """The quantize kernels encode block scales with the hardware fp32 -> E4M3
     conversion; on every fp32 value in [0, 448] it must give the bit-level rule's code
