@@ -494,8 +494,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one piece (c2_step, c2_kernel, c3_kernel, c4a_kernel, "
-                         "c4b_kernel, c5_qlinear, c5_qlinear_act, c5_qlinear_act_given, "
-                         "c5_mx_gemm, copy) and exit")
+                         "c4b_kernel, c2_dequant_bf16, c2_dequant_f32, c2_mx_dequant_bf16, "
+                         "c4a_dequant_hadamard_bf16, c5_qlinear, c5_qlinear_act, "
+                         "c5_qlinear_act_given, c5_mx_gemm, copy) and exit")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -549,6 +550,24 @@ def main():
             y = fos.qlinear_fwd_act(x, wq, x_tensor_scale=t)
             for _ in range(args.steps):
                 fos.qlinear_fwd_act(x, wq, x_tensor_scale=t, out=y)
+            torch.cuda.synchronize()
+            log(f"ran {args.only} x{args.steps}")
+            return
+        if args.only in ("c2_dequant_bf16", "c2_dequant_f32", "c2_mx_dequant_bf16",
+                         "c4a_dequant_hadamard_bf16"):
+            dt = torch.float32 if args.only == "c2_dequant_f32" else torch.bfloat16
+            if args.only == "c2_mx_dequant_bf16":
+                q = fos.mx_quantize(x2.to("cuda:0"))
+                run = lambda: fos.mx_dequantize(q, dt)
+            elif args.only == "c4a_dequant_hadamard_bf16":
+                q = fos.quantize(W.make("c4a").to("cuda:0"), hadamard_seed=0, rounding="sr",
+                                 sr_seed=1234)
+                run = lambda: fos.dequantize(q, dt, inverse_hadamard=True)
+            else:
+                q = fos.quantize(x2.to("cuda:0"))
+                run = lambda: fos.dequantize(q, dt)
+            for _ in range(args.steps):
+                run()
             torch.cuda.synchronize()
             log(f"ran {args.only} x{args.steps}")
             return
