@@ -50,6 +50,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 // over every fp32 value in [0, 448].
 hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t stream);
 
+// Adds to *mismatches the number of disagreements between the hardware E2M1
+// conversion the quantize kernels use and the rounding rule, over every finite fp32.
+hipError_t launch_selftest_e2m1(unsigned long long* mismatches, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
                              int64_t rows, int64_t cols, bool bf16_out, void* out,
                              hipStream_t stream);

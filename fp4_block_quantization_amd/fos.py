@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "fos_quantize_scaled": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
         "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "fos_selftest_e4m3": ([P, P], ctypes.c_int),
+        "fos_selftest_e2m1": ([P, P], ctypes.c_int),
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_dequantize_hadamard": ([P, P, P, I64, I64, ctypes.c_uint64, ctypes.c_int, P, P],
                                     ctypes.c_int),
@@ -163,6 +164,15 @@ def selftest_e4m3(device="cuda:0") -> int:
     correct device."""
     n = torch.zeros(1, dtype=torch.int64, device=device)
     _check(_lib.fos_selftest_e4m3(_ptr(n), _stream(n.device)), "fos_selftest_e4m3")
+    return int(n.item())
+
+
+def selftest_e2m1(device="cuda:0") -> int:
+    """Number of finite fp32 values whose hardware E2M1 conversion (used by the quantize
+    kernels for the element codes) differs from the rounding rule; 0 on a correct
+    device."""
+    n = torch.zeros(1, dtype=torch.int64, device=device)
+    _check(_lib.fos_selftest_e2m1(_ptr(n), _stream(n.device)), "fos_selftest_e2m1")
     return int(n.item())
 
 

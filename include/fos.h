@@ -153,6 +153,17 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
  * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
 fos_status fos_selftest_e4m3(unsigned long long* mismatches, void* stream);
 
+/* Self-test of the hardware E2M1 conversion that the quantize kernels use for the
+ * element codes (gfx950's fp32 -> FP4 conversion with scale 1): adds to *mismatches
+ * (device uint64, 8-byte aligned; the caller zeroes it) the number of finite fp32
+ * values v -- every bit pattern except NaN and Inf -- whose hardware code differs from
+ * the rounding rule: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (Ultralytics glossary
+ * "FP4", opening section), ties to the even code, saturating at 6, with the sign of v
+ * (a value that rounds to 0 keeps it).  A correct device gives 0.  Takes a few tens
+ * of milliseconds.
+ * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream);
+
 /* Dequantize one NVFP4 record: out[r][c] = RN_fp32(E2M1(q) * RN_fp32(E4M3(s) * t))
  * with the nibble's sign (-0 for code 8); FOS_OUT_BF16 rounds that fp32 value to
  * bf16 (nearest-even).  Works for row-wise, column-wise (giving X^T) and 2D records.

@@ -142,6 +142,13 @@ def test_hardware_e4m3_conversion_matches_rule(fos):
     assert fos.selftest_e4m3() == 0
 
 
+def test_hardware_e2m1_conversion_matches_rule(fos):
+    """The quantize kernels round element values to E2M1 with the hardware conversion;
+    on every finite fp32 value it must give the rule's code (nearest, ties to the even
+    code, saturating at 6, sign kept) that the oracle implements."""
+    assert fos.selftest_e2m1() == 0
+
+
 @pytest.mark.parametrize("rows", [1, 3, 7])
 def test_row_wise_any_row_count(fos, rows):
     bits = bits_of(W.random_bf16(rows, 4096 + 48, 55 + rows, "student_t"))
