@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfos.so")
 
-SOURCES = ["amax.hip", "quantize.hip", "dequantize.hip", "qlinear.hip", "mxfp4.hip", "api.cpp"]
+SOURCES = ["amax.hip", "quantize.hip", "dequantize.hip", "qlinear.hip", "mxfp4.hip", "selftest.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 

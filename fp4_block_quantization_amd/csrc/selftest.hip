@@ -1,0 +1,73 @@
+// Device self-tests of the hardware conversions that the quantize kernels use in place
+// of the bit-level rules they stand for (format: Ultralytics glossary "FP4", opening
+// section and "How FP4 works"): fp32 -> E4M3 for the block scales and fp32 -> E2M1
+// for the element codes.  Each kernel runs every input of its range through both and
+// adds the number of disagreements to a device counter.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace fos {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Self-test of the hardware E4M3 conversion: every fp32 bit pattern in [0, 448] is
+// converted by e4m3_encode_pk_hw (both halves) and by e4m3_encode; each lane counts
+// its disagreements and adds a nonzero count to *mismatches.
+constexpr uint32_t kE4m3TestPatterns = 0x43E00001u;   // +0 .. 448.0 inclusive
+__global__ __launch_bounds__(kThreads) void selftest_e4m3_kernel(unsigned long long* mismatches) {
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t bad = 0;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < kE4m3TestPatterns; i += stride) {
+    const float r = __uint_as_float(i);
+    const uint32_t hw = e4m3_encode_pk_hw(r, r);
+    const uint32_t sw = e4m3_encode(r);
+    bad += ((hw & 0xffu) != sw) + ((hw >> 8) != sw);
+  }
+  if (bad) atomicAdd(mismatches, (unsigned long long)bad);
+}
+
+// Self-test of the hardware E2M1 conversion (cvt_pk_fp4, scale 1) against the rule it
+// stands for: nearest value of {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,
+// saturating at 6, the sign of v kept (also when the value rounds to 0).  Code k + 1
+// wins over code k when |v| lies above their midpoint, or on it with k + 1 even.
+// Every finite fp32 bit pattern is checked (grid-stride over all 2^32, NaN and Inf
+// skipped); each lane adds a nonzero disagreement count to *mismatches.
+__device__ __forceinline__ uint32_t e2m1_encode_rule(float v) {
+  const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  const float m = fabsf(v);
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k)
+    if (m > mid[k] || (m == mid[k] && ((k + 1) & 1) == 0)) c = k + 1;
+  return c | (__builtin_signbit(v) ? 8u : 0u);
+}
+__global__ __launch_bounds__(kThreads) void selftest_e2m1_kernel(unsigned long long* mismatches) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint32_t bad = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < ((uint64_t)1 << 32);
+       i += stride) {
+    const uint32_t b = (uint32_t)i;
+    if ((b & 0x7f800000u) == 0x7f800000u) continue;   // NaN, Inf
+    const float v = __uint_as_float(b);
+    const uint32_t hw = cvt_pk_fp4<0>(0u, v, v) & 0xffu;
+    const uint32_t sw = e2m1_encode_rule(v);
+    bad += ((hw & 0xfu) != sw) + ((hw >> 4) != sw);
+  }
+  if (bad) atomicAdd(mismatches, (unsigned long long)bad);
+}
+
+}  // namespace
+
+hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t s) {
+  selftest_e4m3_kernel<<<4096, kThreads, 0, s>>>(mismatches);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_e2m1(unsigned long long* mismatches, hipStream_t s) {
+  selftest_e2m1_kernel<<<8192, kThreads, 0, s>>>(mismatches);
+  return hipGetLastError();
+}
+
+}  // namespace fos
