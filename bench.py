@@ -516,7 +516,7 @@ def main():
     if not args.no_cpu and args.only is None:
         log("CPU oracle baseline ...")
         cpu = cpu_baseline(x2, x2.shape[0])
-        workers = max(1, min(16, os.cpu_count() or 1))   # the GPU machine's CPU share is 16
+        workers = max(1, min(16, os.cpu_count() or 1))   # one GPU's share of the host cores
         log(f"CPU oracle on {workers} processes, CPU fp32 matmul ...")
         mc, mm = cpu_baselines_extra(x2, W.make("c5_x"), W.make("c5_w"), workers)
         cpu_rows = {"cpu_oracle_multicore": mc, "cpu_fp32_matmul_c5_slice": mm}
