@@ -14,8 +14,8 @@
 //                      reads two adjacent 16-row column blocks as 16 dwords.
 //   quant_2d_kernel    16x16 tiles: the 16 lanes of a DPP row hold the 16 rows of a
 //                      tile (two tile rows per workgroup); tile max and error sums use
-//                      DPP row permutes; column-wise output is the LDS transpose of the
-//                      same nibbles.
+//                      DPP row permutes; row-wise output goes out through LDS in whole
+//                      lines; column-wise output is the LDS transpose of the same nibbles.
 // Every workgroup first finishes the tensor scale (from the scale pass's partial
 // maxima, or the caller's t) and builds a table of (d, 1/d) for all E4M3 codes.
 #include "device_common.hpp"
@@ -223,6 +223,13 @@ constexpr int k2dTileRows = 2;
 template <bool k46, bool kSR, bool kRows, bool kCols>
 __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   __shared__ uint2 tr[k2dTileRows][16][17];
+  // row-wise outputs of the workgroup, staged so that the global stores cover whole
+  // lines: [tile row][row][tile] nibbles (a row of 16 tiles is 128 contiguous bytes)
+  // and scale bytes (16 contiguous bytes).  Stored directly, each wave instruction
+  // wrote 16 rows x 32 bytes of nibbles and 16 rows x 4 bytes of scales; staged, 8
+  // threads write one 128-byte line, with non-temporal stores like the row-wise kernel.
+  __shared__ uint2 rnib[kRows ? k2dTileRows : 1][16][16];
+  __shared__ uint8_t rsc[kRows ? k2dTileRows : 1][16][16];
   const int64_t R = a.rows, C = a.cols;
   const uint32_t tiles_c = (uint32_t)(C / 16);
   const uint32_t wg_per_row = (tiles_c + 15) / 16;
@@ -270,7 +277,10 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
       c4.err = row16_sum(c4.err);
       if (c4.err < c6.err) c = c4;
     }
-    if (kRows && valid) store_block(a.row_data, a.row_scales, 8 * rblk, rblk, c);
+    if (kRows) {
+      rnib[q][row][tl] = make_uint2(c.lo, c.hi);
+      rsc[q][row][tl] = (uint8_t)c.s;
+    }
     if (kCols) {
       tr[q][tl][row] = make_uint2(c.lo, c.hi);
       __syncthreads();
@@ -288,6 +298,46 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
         const int64_t cblk = col * (R / 16) + Rq / 16;
         *reinterpret_cast<uint2*>(a.col_data + 8 * cblk) = make_uint2(lo, hi);
         a.col_scales[cblk] = (uint8_t)c.s;
+      }
+    }
+  }
+  if (kRows) {
+    __syncthreads();
+    // thread t stores tiles 2j, 2j + 1 (16 bytes of nibbles) of row r of tile row q
+    const int q = tid >> 7, r = (tid >> 3) & 15, j = tid & 7;
+    const int64_t gr = R0 + 16 * q + r;
+    const uint32_t T0 = (blockIdx.x % wg_per_row) * 16;
+    const uint32_t t0 = T0 + 2 * j;
+    if (gr < R && t0 < tiles_c) {
+      uint8_t* dst = a.row_data + gr * (C / 2) + 8 * (int64_t)t0;
+      const uint2 n0 = rnib[q][r][2 * j];
+      if (t0 + 1 < tiles_c) {
+        const uint2 n1 = rnib[q][r][2 * j + 1];
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(v4u{n0.x, n0.y, n1.x, n1.y}, reinterpret_cast<v4u*>(dst));
+        }
+        else {
+          *reinterpret_cast<uint2*>(dst) = n0;
+          *reinterpret_cast<uint2*>(dst + 8) = n1;
+        }
+      } else {
+        *reinterpret_cast<uint2*>(dst) = n0;
+      }
+    }
+    // threads 0-31 store the 16 scale bytes of row r of tile row q
+    if (tid < 16 * k2dTileRows) {
+      const int qs = tid >> 4, rs = tid & 15;
+      const int64_t grs = R0 + 16 * qs + rs;
+      if (grs < R) {
+        uint8_t* dst = a.row_scales + grs * (C / 16) + T0;
+        if (T0 + 16 <= tiles_c && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+          const uint4 sv = *reinterpret_cast<const uint4*>(&rsc[qs][rs][0]);
+          __builtin_nontemporal_store(v4u{sv.x, sv.y, sv.z, sv.w}, reinterpret_cast<v4u*>(dst));
+        } else {
+          for (uint32_t t = 0; t < 16 && T0 + t < tiles_c; ++t) dst[t] = rsc[qs][rs][t];
+        }
       }
     }
   }
