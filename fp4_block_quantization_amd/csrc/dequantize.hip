@@ -8,7 +8,7 @@
 // reads the 2 or 4 nibble bytes of its chunk (contiguous across lanes) and the block's
 // scale byte (shared by the 4 or 2 lanes of a block).  Hardware E2M1 -> fp32
 // conversion; bf16 output rounds the fp32 value to nearest-even.  The inverse-Hadamard
-// variant needs whole blocks per lane (32 or 64 bytes out per lane).
+// variant needs whole blocks per lane and stages its outputs through LDS.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -78,40 +78,58 @@ __device__ __forceinline__ void dequant_block(uint2 q, uint32_t s, float t, floa
   }
 }
 
-// Store block b's 16 values: 32 bytes of bf16 (RNE) or 64 bytes of fp32.
-template <bool kBF16>
-__device__ __forceinline__ void store_values(void* out, int64_t b, const float (&v)[16]) {
-  // cached stores: each instruction writes 16 bytes at a 32- or 64-byte stride, and L2
-  // merges the pieces of a line (non-temporal stores measured slower here)
-  if (kBF16) {
-    uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      o[h] = make_uint4(pack_bf16x2(v[8 * h + 0], v[8 * h + 1]), pack_bf16x2(v[8 * h + 2], v[8 * h + 3]),
-                        pack_bf16x2(v[8 * h + 4], v[8 * h + 5]), pack_bf16x2(v[8 * h + 6], v[8 * h + 7]));
-  } else {
-    float4* o = reinterpret_cast<float4*>(out) + 4 * b;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) o[h] = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
-  }
-}
-
 // Records made with the random Hadamard transform, returned to the original basis:
 // lane = one 16-value block (8 nibble bytes + 1 scale byte in, 32 or 64 bytes out);
 // values are dequantized exactly as above, then inverse-transformed in registers.
+// A workgroup's 256 blocks are contiguous in the output, so their values go through
+// LDS and out as 16-byte chunks that are contiguous across lanes: every store
+// instruction of a wave writes 1 KB of whole lines (non-temporal, as in the
+// output-major kernel).  Stored from the lanes that computed them, each instruction
+// wrote 16 bytes at a 32- or 64-byte stride.
 template <bool kBF16>
 __global__ __launch_bounds__(kThreads) void dequant_rht_kernel(const uint2* __restrict__ data,
                                                                const uint8_t* __restrict__ scales,
                                                                const float* __restrict__ tscale,
                                                                int64_t nblk, uint32_t mask,
                                                                void* __restrict__ out) {
+  constexpr int kChunks = kBF16 ? 2 : 4;      // 16-byte output chunks per block
+  __shared__ uint4 stage[kThreads * kChunks];
   const float t = tscale[0];
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    float v[16];
-    dequant_block(data[b], scales[b], t, v);
-    irht16(v, mask);
-    store_values<kBF16>(out, b, v);
+  uint4* __restrict__ o = reinterpret_cast<uint4*>(out);
+  for (int64_t b0 = (int64_t)blockIdx.x * kThreads; b0 < nblk; b0 += stride) {  // uniform
+    const int64_t b = b0 + threadIdx.x;
+    if (b < nblk) {
+      float v[16];
+      dequant_block(data[b], scales[b], t, v);
+      irht16(v, mask);
+      uint4* st = stage + threadIdx.x * kChunks;
+      if (kBF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          st[h] = make_uint4(pack_bf16x2(v[8 * h + 0], v[8 * h + 1]),
+                             pack_bf16x2(v[8 * h + 2], v[8 * h + 3]),
+                             pack_bf16x2(v[8 * h + 4], v[8 * h + 5]),
+                             pack_bf16x2(v[8 * h + 6], v[8 * h + 7]));
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          st[h] = make_uint4(__float_as_uint(v[4 * h]), __float_as_uint(v[4 * h + 1]),
+                             __float_as_uint(v[4 * h + 2]), __float_as_uint(v[4 * h + 3]));
+      }
+    }
+    __syncthreads();
+    const int64_t nchunk = min((int64_t)kThreads, nblk - b0) * kChunks;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = threadIdx.x + kThreads * j;
+      if (c < nchunk) {
+        const uint4 w = stage[c];
+        __builtin_nontemporal_store(v4u{w.x, w.y, w.z, w.w},
+                                    reinterpret_cast<v4u*>(o + b0 * kChunks + c));
+      }
+    }
+    __syncthreads();   // the next iteration overwrites the stage
   }
 }
 

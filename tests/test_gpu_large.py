@@ -144,6 +144,28 @@ def test_dequantize_past_2_31(fos, big, dtype):
     del y, data, scales
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_hadamard_past_2_31(fos, big, dtype):
+    """Inverse-Hadamard dequantize of a random record of the same shape: the kernel's
+    workgroups loop over many 256-block ranges; sampled rows against the oracle."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    data = torch.randint(0, 256, (R, C // 2), generator=g, device=DEV, dtype=torch.uint8)
+    scales = torch.randint(0, 127, (R, C // 16), generator=g, device=DEV, dtype=torch.uint8)
+    t = np.float32(0.0071)
+    rec = fos.NVFP4Tensor(data, scales, torch.tensor([t], dtype=torch.float32, device=DEV),
+                          hadamard_seed=11)
+    y = fos.dequantize(rec, dtype, inverse_hadamard=True)
+    rows = _rows(12, 8)
+    want = N.dequantize_hadamard(_host_rows(data, rows), _host_rows(scales, rows), t, 11)
+    got = _host_rows(y.view(torch.int32 if dtype == torch.float32 else torch.int16), rows)
+    if dtype == torch.float32:
+        _same(got.view(np.uint32), want.view(np.uint32), "deq-rht f32")
+    else:
+        _same(got.view(np.uint16), F.f32_to_bf16_bits(want), "deq-rht bf16")
+    del y, data, scales
+
+
 def test_mxfp4_past_2_31(fos, big):
     """The same elements as a [65544, 32800] tensor (MXFP4 rows are whole 32-blocks)."""
     x, bits, _ = big
