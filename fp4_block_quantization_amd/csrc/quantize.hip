@@ -11,7 +11,9 @@
 //   quant_tile_kernel  column-wise output (optionally row-wise from the same read):
 //                      a 128x64 tile goes through LDS (XOR-swizzled 16-byte groups,
 //                      so the column reads spread over the banks); each lane then
-//                      reads two adjacent 16-row column blocks as 16 dwords.
+//                      reads two adjacent 16-row column blocks as 16 dwords.  With
+//                      row-wise output a workgroup walks 4 tiles along its rows and
+//                      writes the row-wise record through LDS in whole lines.
 //   quant_2d_kernel    16x16 tiles: the 16 lanes of a DPP row hold the 16 rows of a
 //                      tile (two tile rows per workgroup); tile max and error sums use
 //                      DPP row permutes; row-wise output goes out through LDS in whole
@@ -109,87 +111,146 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
 // columns (two 16-byte loads per row), quantizes those row blocks from registers
 // (row-wise output) and writes them to LDS; after one barrier each lane reads 16-row
 // column pieces back and quantizes TR/64 column blocks.
+//
+// With row-wise output, a workgroup walks kRowSub tiles along its rows (TR x 256
+// columns) and stages the row-wise nibbles and scale bytes in LDS: a row's 16 blocks
+// are 128 contiguous bytes of nibbles, written at the end as whole lines with
+// non-temporal stores (stored per tile, each wave instruction wrote 16 rows x 32
+// bytes, and those row-wise stores took a quarter of the kernel's time).  The next
+// tile's loads are issued before the current tile's column phase.
 constexpr int kTileC = 64;
 constexpr int kColTileRows = 128;  // rows of a column-wise tile
+constexpr int kRowSub = 4;         // tiles along a row per workgroup with row-wise output
 
 template <int TR, bool k46, bool kSR, bool kRHT, bool kRows>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
+  constexpr int kSub = kRows ? kRowSub : 1;
   constexpr int kIt = TR / 64;          // rows per lane in the load phase
   constexpr int kNRB = TR / 16;         // 16-row blocks per tile
   constexpr int kLanesPerRB = kThreads / kNRB;
   constexpr int kH = 32 / kLanesPerRB;  // dword columns (column pairs) per lane
+  constexpr int kRowBlocks = 4 * kSub;  // row blocks per row of the workgroup
   // TR rows x 32 dwords (64 bf16); logical dword q of row r lives at q ^ sw(r),
   // sw(r) = 4 * ((r >> 4) & 7).
   __shared__ uint32_t lds[TR * 32];
+  __shared__ uint2 rnib[kRows ? TR : 1][kRows ? kRowBlocks : 1];
+  __shared__ uint8_t rsc[kRows ? TR : 1][kRows ? kRowBlocks : 1];
   const int64_t R = a.rows, C = a.cols;
-  const int64_t tiles_c = (C + kTileC - 1) / kTileC;
-  const int64_t R0 = (int64_t)(blockIdx.x / tiles_c) * TR;
-  const int64_t C0 = (int64_t)(blockIdx.x % tiles_c) * kTileC;
+  const int64_t span = (int64_t)kTileC * kSub;
+  const int64_t wg_c = (C + span - 1) / span;
+  const int64_t R0 = (int64_t)(blockIdx.x / wg_c) * TR;
+  const int64_t CW = (int64_t)(blockIdx.x % wg_c) * span;   // first column of the workgroup
   const int tid = threadIdx.x;
-
-  // all of the lane's 16-byte loads are in flight before anything waits on them
   const int j = tid & 3;
+
+  // all of the lane's 16-byte loads of a tile are in flight before anything waits on them
   uint4 w[2 * kIt];
+  auto load_tile = [&](int64_t C0) {
 #pragma unroll
-  for (int k = 0; k < kIt; ++k) {
-    const int row = (tid >> 2) + 64 * k;
-    const int64_t gr = R0 + row, gc = C0 + 16 * j;
-    w[2 * k] = make_uint4(0, 0, 0, 0);
-    w[2 * k + 1] = w[2 * k];
-    if (gr < R && gc < C) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
-      w[2 * k] = p[0];
-      w[2 * k + 1] = p[1];
+    for (int k = 0; k < kIt; ++k) {
+      const int row = (tid >> 2) + 64 * k;
+      const int64_t gr = R0 + row, gc = C0 + 16 * j;
+      w[2 * k] = make_uint4(0, 0, 0, 0);
+      w[2 * k + 1] = w[2 * k];
+      if (gr < R && gc < C) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
+        w[2 * k] = p[0];
+        w[2 * k + 1] = p[1];
+      }
     }
-  }
+  };
+  load_tile(CW);
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab);
-#pragma unroll
-  for (int k = 0; k < kIt; ++k) {
-    const int row = (tid >> 2) + 64 * k;
-    const int64_t gr = R0 + row, gc = C0 + 16 * j;
-    const bool ok = gr < R && gc < C;
-    const uint4 w0 = w[2 * k], w1 = w[2 * k + 1];
-    const int sw = 4 * ((row >> 4) & 7);
-    *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j) ^ sw)]) = w0;
-    *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j + 4) ^ sw)]) = w1;
-    if (kRows && ok) {
-      float v[16];
-      unpack16(w0, w1, v);
-      float srq[16];
-      const int64_t blk = gr * (C / 16) + gc / 16;
-      if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srq);
-      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
-      store_block(a.row_data, a.row_scales, 8 * blk, blk, c);
-    }
-  }
-  __syncthreads();
 
-  const int rb = tid % kNRB;
-  const int sw = 4 * (rb & 7);
-  const int64_t nrb = R / 16;
+#pragma unroll 1
+  for (int s = 0; s < kSub; ++s) {
+    const int64_t C0 = CW + (int64_t)kTileC * s;
+    if (C0 >= C) break;                          // uniform across the workgroup
 #pragma unroll
-  for (int h = 0; h < kH; ++h) {
-    const int p = tid / kNRB + kLanesPerRB * h;
-    const int64_t gr0 = R0 + 16 * rb, gc = C0 + 2 * p;
-    if (gr0 >= R || gc >= C) continue;
-    float va[16], vb[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t w = lds[(16 * rb + i) * 32 + (p ^ sw)];
-      va[i] = bf16_lo(w);
-      vb[i] = bf16_hi(w);
+    for (int k = 0; k < kIt; ++k) {
+      const int row = (tid >> 2) + 64 * k;
+      const int64_t gr = R0 + row, gc = C0 + 16 * j;
+      const uint4 w0 = w[2 * k], w1 = w[2 * k + 1];
+      const int sw = 4 * ((row >> 4) & 7);
+      *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j) ^ sw)]) = w0;
+      *reinterpret_cast<uint4*>(&lds[row * 32 + ((8 * j + 4) ^ sw)]) = w1;
+      if (kRows && gr < R && gc < C) {
+        float v[16];
+        unpack16(w0, w1, v);
+        float srq[16];
+        const int64_t blk = gr * (C / 16) + gc / 16;
+        if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srq);
+        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
+        rnib[row][4 * s + j] = make_uint2(c.lo, c.hi);
+        rsc[row][4 * s + j] = (uint8_t)c.s;
+      }
     }
+    if (s + 1 < kSub) load_tile(C0 + kTileC);
+    __syncthreads();
+
+    const int rb = tid % kNRB;
+    const int sw = 4 * (rb & 7);
+    const int64_t nrb = R / 16;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float (&v)[16] = s ? vb : va;
-      const int64_t col = gc + s;
-      if (kRHT) rht16(v, a.rht_mask);
-      const int64_t blk = col * nrb + gr0 / 16;
-      float srq[16];
-      if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srq);
-      const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
-      store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
+    for (int h = 0; h < kH; ++h) {
+      const int p = tid / kNRB + kLanesPerRB * h;
+      const int64_t gr0 = R0 + 16 * rb, gc = C0 + 2 * p;
+      if (gr0 >= R || gc >= C) continue;
+      float va[16], vb[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t wd = lds[(16 * rb + i) * 32 + (p ^ sw)];
+        va[i] = bf16_lo(wd);
+        vb[i] = bf16_hi(wd);
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        float (&v)[16] = t2 ? vb : va;
+        const int64_t col = gc + t2;
+        if (kRHT) rht16(v, a.rht_mask);
+        const int64_t blk = col * nrb + gr0 / 16;
+        float srq[16];
+        if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srq);
+        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
+        store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
+      }
+    }
+    // the next tile overwrites the LDS tile; the row-wise flush reads other lanes' rows
+    if (kRows || s + 1 < kSub) __syncthreads();
+  }
+
+  if (kRows) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const int64_t vb = min(span, C - CW) / 16;      // valid row blocks per row
+    constexpr int kChunks = kRowBlocks / 2;        // 16-byte chunks of nibbles per row
+#pragma unroll
+    for (int it = 0; it < TR * kChunks / kThreads; ++it) {
+      const int ch = tid + kThreads * it;
+      const int row = ch / kChunks, b0 = 2 * (ch % kChunks);
+      const int64_t gr = R0 + row;
+      if (gr >= R || b0 >= vb) continue;
+      uint8_t* dst = a.row_data + gr * (C / 2) + CW / 2 + 8 * b0;
+      const uint2 n0 = rnib[row][b0];
+      if (b0 + 1 < vb && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        const uint2 n1 = rnib[row][b0 + 1];
+        __builtin_nontemporal_store(v4u{n0.x, n0.y, n1.x, n1.y}, reinterpret_cast<v4u*>(dst));
+      } else {
+        *reinterpret_cast<uint2*>(dst) = n0;
+        if (b0 + 1 < vb) *reinterpret_cast<uint2*>(dst + 8) = rnib[row][b0 + 1];
+      }
+    }
+    if (tid < TR) {
+      const int64_t gr = R0 + tid;
+      if (gr < R) {
+        uint8_t* dst = a.row_scales + gr * (C / 16) + CW / 16;
+        if (vb == kRowBlocks && kRowBlocks == 16 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          const uint4 sv = *reinterpret_cast<const uint4*>(&rsc[tid][0]);
+          __builtin_nontemporal_store(v4u{sv.x, sv.y, sv.z, sv.w}, reinterpret_cast<v4u*>(dst));
+        } else {
+          for (int b = 0; b < vb; ++b) dst[b] = rsc[tid][b];
+        }
+      }
     }
   }
 }
@@ -383,7 +444,8 @@ int64_t quantize_grid(const QuantArgs& a) {
   if (a.two_d)  // k2dTileRows tile rows x 16 tile columns per workgroup
     return ((a.rows / 16 + k2dTileRows - 1) / k2dTileRows) * ((a.cols / 16 + 15) / 16);
   if (!a.cols_out) return (a.rows * a.cols / 16 + kRowsPerWG - 1) / kRowsPerWG;
-  return ((a.rows + kColTileRows - 1) / kColTileRows) * ((a.cols + kTileC - 1) / kTileC);
+  const int64_t span = (int64_t)kTileC * (a.rows_out ? kRowSub : 1);
+  return ((a.rows + kColTileRows - 1) / kColTileRows) * ((a.cols + span - 1) / span);
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
