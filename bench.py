@@ -192,7 +192,11 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.0):
         settle(case.step, sets, settle_s)
     ms = time_loop(case.step, steps, warmup, sets)
     ms_k_eager = time_loop(case.scaled, steps, warmup, sets)
-    ms_k = graph_loop(case.on_stream, steps, warmup, sets)
+    try:
+        ms_k, timing = graph_loop(case.on_stream, steps, warmup, sets), "hip_graph_replay"
+    except RuntimeError as exc:    # capture unavailable: fall back to the eager calls
+        log(f"{name}: graph capture failed ({exc}); kernel time from eager calls")
+        ms_k, timing = ms_k_eager, "eager_calls"
     ms_a = time_loop(case.scale_only, steps, warmup, sets)
     if case.bad:
         raise RuntimeError(f"{name}: a fos call returned an error status")
@@ -203,7 +207,7 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.0):
            "frac_step": b / ms / 1e6 / HBM_PEAK_GBS,
            "ms_quant_kernel": ms_k, "GBps_quant_kernel": b / ms_k / 1e6,
            "frac_quant_kernel": b / ms_k / 1e6 / HBM_PEAK_GBS,
-           "ms_quant_kernel_eager_calls": ms_k_eager,
+           "ms_quant_kernel_eager_calls": ms_k_eager, "quant_kernel_timing": timing,
            "ms_scale_kernel": ms_a, "GBps_scale_kernel": 2 * R * C / ms_a / 1e6}
     del case
     return row
