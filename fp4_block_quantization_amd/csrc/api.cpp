@@ -273,6 +273,15 @@ fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream) {
              : FOS_E_HIP;
 }
 
+fos_status fos_selftest_e2m1_sr(unsigned long long* mismatches, void* stream) {
+  if (!mismatches) return FOS_E_NULL;
+  if (!aligned(mismatches, 8)) return FOS_E_ALIGN;
+  return fos::launch_selftest_e2m1_sr(mismatches, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
 fos_status fos_dequantize(const uint8_t* data, const uint8_t* scales, const float* tensor_scale,
                           int64_t rows, int64_t cols, int out_dtype, void* out, void* stream) {
   const fos_status st = check_dequantize(data, scales, tensor_scale, rows, cols, out_dtype, out);

@@ -149,33 +149,65 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-// Stochastic-rounding draws of one block: byte k_i of the 16 Philox output bytes,
-// returned as the threshold q_i = (k_i + 0.5) / 256 (exact in fp32).  Counter =
-// (b_lo, b_hi, 0, stream).
-__device__ __forceinline__ void sr_draws(uint64_t block, uint32_t stream, uint32_t k0,
-                                         uint32_t k1, float (&q)[16]) {
+// ---- stochastic rounding on the hardware conversion --------------------------------
+// The draw rule: with lo and hi the E2M1 values around |v| (6 and above give 6) and
+// p = (|v| - lo) / (hi - lo) exact, |v| rounds up to hi iff q < p, q = (k + 0.5) / 256
+// for the element's draw byte k.
+//
+// v_cvt_scalef32_sr_pk_fp4_f32 rounds the first value of its pair under a 32-bit
+// operand R: it keeps 22 fraction bits of p (p22; the bits of |v| below them are
+// dropped) and the top 22 bits of R (R22), and rounds up iff p22 + R22 / 2^22 >= 1
+// (saturating at 6, the sign of v kept).  p has more than 22 bits only for |v| < 1,
+// where fp32 resolves |v| more finely than 2^-22 of the 0.5 grid step.
+//
+// With R = (~k << 24) | 0x7fffff, R22 = 2^22 (1 - q) - 1 and the hardware rounds up
+// iff p22 > q (q is a multiple of 2^-9).  That is the rule except when p22 == q and p
+// has dropped bits, where the rule rounds up.  In that case |v| lies less than 2^-23
+// above a multiple of 2^-10 and is at least 2^-10 (q >= 2^-9), so the dropped bits are
+// exactly the ten lowest bits of v's pattern, not all zero; for |v| >= 1, p == q needs
+// |v| a multiple of 2^-10, whose ten lowest bits are zero.  Adding those ten bits to R
+// (whose own ten lowest bits are ones) raises R22 by one exactly when they are
+// nonzero: that turns the hardware's decision at p22 == q into the rule's and leaves
+// every other decision alone.  fos_selftest_e2m1_sr checks the result on the device
+// for every finite fp32 value and every k.
+//
+// Operands of one block: byte i of the block's Philox output (counter
+// (b_lo, b_hi, 0, stream)) is element i's draw k_i; r_i = (~k_i << 24) | 0x7fffff.
+template <int B>
+__device__ __forceinline__ uint32_t sr_operand(uint32_t nw) {   // nw = ~(Philox word)
+  return __builtin_amdgcn_perm(nw, 0x007fffffu, 0x04020100u + ((uint32_t)B << 24));
+}
+__device__ __forceinline__ void sr_operands(uint64_t block, uint32_t stream, uint32_t k0,
+                                            uint32_t k1, uint32_t (&r)[16]) {
   const uint4 w = philox4x32_10(make_uint4((uint32_t)block, (uint32_t)(block >> 32), 0u, stream),
                                 k0, k1);
-  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t nw[4] = {~w.x, ~w.y, ~w.z, ~w.w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    q[i] = __builtin_fmaf((float)((words[i >> 2] >> (8 * (i & 3))) & 0xffu), 0x1p-8f, 0x1p-9f);
+  for (int m = 0; m < 4; ++m) {
+    r[4 * m + 0] = sr_operand<0>(nw[m]);
+    r[4 * m + 1] = sr_operand<1>(nw[m]);
+    r[4 * m + 2] = sr_operand<2>(nw[m]);
+    r[4 * m + 3] = sr_operand<3>(nw[m]);
+  }
+}
+// The stochastic code of a under its element's r, in the low nibble of byte 0 of the
+// result; every other bit of the result is unspecified (the high nibble holds b
+// rounded under a's operand; the instruction leaves bytes 1..3 of its destination
+// register as they were, and the compiler does not load the builtin's `old` operand
+// into that register).  Scale operand 1.0 = no scaling.
+__device__ __forceinline__ uint32_t cvt_sr_fp4(float a, float b, uint32_t r) {
+  const f32x2 v = {a, b};
+  const uint32_t op = r + (__float_as_uint(a) & 0x3ffu);
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, op, 1.0f, 0);
+}
+// Byte 0 of w0, w1, w2, w3 -> bytes 0, 1, 2, 3 of the result.
+__device__ __forceinline__ uint32_t gather_byte0(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                 uint32_t w3) {
+  const uint32_t t01 = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);
+  const uint32_t t23 = __builtin_amdgcn_perm(w3, w2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
 }
 
-// Stochastic rounding of f = |v| >= 0 onto the E2M1 magnitudes; returns the grid
-// value.  With e = max(exponent of f, 1) (f = m 2^e, m in [0.5, 1)), y = f 2^(2-e)
-// maps f's grid interval ([0,2), [2,4) or [4,6]) onto unit spacing, so y = yl + p
-// with p the exact fractional position.  Rounding up iff q < p (q = (k + 0.5)/256)
-// is ceil(y - q): it gives yl + 1 when p > q and yl when p <= q.  y - q is exact
-// whenever it lies near an integer (y >= 1 has no bits below 2^-22 and q is a
-// multiple of 2^-9; for y < 1 the result stays strictly inside (-1, 1)), so its
-// fp32 rounding never moves the ceiling.  Saturates at 6.
-__device__ __forceinline__ float e2m1_sr_mag(float f, float q) {
-  f = fminf(f, 6.0f);
-  const int e = max(__builtin_amdgcn_frexp_expf(f), 1);
-  const float y = __builtin_ldexpf(f, 2 - e);
-  return __builtin_ldexpf(__builtin_ceilf(y - q), e - 2);
-}
 // ---- random-sign 16-point Hadamard transform ---------------------------------------
 // Butterflies with strides 1, 2, 4, 8: (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h); the
 // result is H16 y (Sylvester order).
@@ -291,29 +323,39 @@ __device__ __forceinline__ void cand_codes_rne(const float (&x)[16], float d, fl
   c.err = err;
 }
 
-// Stochastic-rounding codes and the sequential squared error.  Each value is first
-// rounded to an exact grid value (with x's sign, so that values rounding to zero
-// keep it); the hardware RNE conversion of an exact grid value is that value's code.
+// Stochastic-rounding codes (hardware conversion under the draws' operands, see above)
+// and the sequential squared error of the decoded values.  Element 2j's code comes
+// from the pair (v_2j, v_2j+1), element 2j+1's from the swapped pair; the codes are
+// gathered byte by byte and merged nibble by nibble.
 __device__ __forceinline__ void cand_codes_sr(const float (&x)[16], float d, float inv,
-                                              const float (&q)[16], Cand& c) {
-  float g[16];
+                                              const uint32_t (&r)[16], Cand& c) {
+  float v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    g[i] = __builtin_copysignf(e2m1_sr_mag(fabsf(x[i] * inv), q[i]), x[i]);
-  uint32_t lo = 0, hi = 0;
-  lo = cvt_pk_fp4<0>(lo, g[0], g[1]);
-  lo = cvt_pk_fp4<1>(lo, g[2], g[3]);
-  lo = cvt_pk_fp4<2>(lo, g[4], g[5]);
-  lo = cvt_pk_fp4<3>(lo, g[6], g[7]);
-  hi = cvt_pk_fp4<0>(hi, g[8], g[9]);
-  hi = cvt_pk_fp4<1>(hi, g[10], g[11]);
-  hi = cvt_pk_fp4<2>(hi, g[12], g[13]);
-  hi = cvt_pk_fp4<3>(hi, g[14], g[15]);
+  for (int i = 0; i < 16; ++i) v[i] = x[i] * inv;
+  uint32_t ev[8], od[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ev[j] = cvt_sr_fp4(v[2 * j], v[2 * j + 1], r[2 * j]);
+    od[j] = cvt_sr_fp4(v[2 * j + 1], v[2 * j], r[2 * j + 1]);
+  }
+  const uint32_t e0 = gather_byte0(ev[0], ev[1], ev[2], ev[3]);
+  const uint32_t o0 = gather_byte0(od[0], od[1], od[2], od[3]);
+  const uint32_t e1 = gather_byte0(ev[4], ev[5], ev[6], ev[7]);
+  const uint32_t o1 = gather_byte0(od[4], od[5], od[6], od[7]);
+  const uint32_t lo = (e0 & 0x0f0f0f0fu) | ((o0 << 4) & 0xf0f0f0f0u);
+  const uint32_t hi = (e1 & 0x0f0f0f0fu) | ((o1 << 4) & 0xf0f0f0f0u);
+  f32x2 e[8];
+  e[0] = cvt_pk_f32_fp4<0>(lo); e[1] = cvt_pk_f32_fp4<1>(lo);
+  e[2] = cvt_pk_f32_fp4<2>(lo); e[3] = cvt_pk_f32_fp4<3>(lo);
+  e[4] = cvt_pk_f32_fp4<0>(hi); e[5] = cvt_pk_f32_fp4<1>(hi);
+  e[6] = cvt_pk_f32_fp4<2>(hi); e[7] = cvt_pk_f32_fp4<3>(hi);
   float err = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float e = __builtin_fmaf(g[i], d, -x[i]);
-    err = __builtin_fmaf(e, e, err);
+  for (int j = 0; j < 8; ++j) {
+    const float d0 = __builtin_fmaf(e[j].x, d, -x[2 * j]);
+    err = __builtin_fmaf(d0, d0, err);
+    const float d1 = __builtin_fmaf(e[j].y, d, -x[2 * j + 1]);
+    err = __builtin_fmaf(d1, d1, err);
   }
   c.lo = lo;
   c.hi = hi;
@@ -344,16 +386,16 @@ __device__ __forceinline__ float amax16(const float (&x)[16]) {
 // Quantize one 1D block with both candidates (or 6 alone) and return the winner.
 template <bool kFourOverSix, bool kSR>
 __device__ __forceinline__ Cand quantize_block(const float (&x)[16], const float2* tab,
-                                               float u6, float u4, const float (&srq)[16]) {
+                                               float u6, float u4, const uint32_t (&srr)[16]) {
   const float a = amax16(x);
   Cand c6, c4;
   float inv6, inv4;
   cand_scale_bytes(a, u6, u4, c6.s, c4.s);
   cand_lookup(c6.s, tab, c6.d, inv6);
-  if (kSR) cand_codes_sr(x, c6.d, inv6, srq, c6); else cand_codes_rne(x, c6.d, inv6, c6);
+  if (kSR) cand_codes_sr(x, c6.d, inv6, srr, c6); else cand_codes_rne(x, c6.d, inv6, c6);
   if (!kFourOverSix) return c6;
   cand_lookup(c4.s, tab, c4.d, inv4);
-  if (kSR) cand_codes_sr(x, c4.d, inv4, srq, c4); else cand_codes_rne(x, c4.d, inv4, c4);
+  if (kSR) cand_codes_sr(x, c4.d, inv4, srr, c4); else cand_codes_rne(x, c4.d, inv4, c4);
   return (c4.err < c6.err) ? c4 : c6;
 }
 

@@ -54,6 +54,11 @@ hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t stre
 // conversion the quantize kernels use and the rounding rule, over every finite fp32.
 hipError_t launch_selftest_e2m1(unsigned long long* mismatches, hipStream_t stream);
 
+// Adds to *mismatches the number of disagreements between the hardware stochastic
+// rounding to E2M1 under the operands the quantize kernels build from their draws and
+// the draw rule, over every finite fp32 and every draw byte.
+hipError_t launch_selftest_e2m1_sr(unsigned long long* mismatches, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
                              int64_t rows, int64_t cols, bool bf16_out, void* out,
                              hipStream_t stream);

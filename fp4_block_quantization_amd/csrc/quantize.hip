@@ -99,9 +99,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
     float v[16];
     unpack16(w[2 * q], w[2 * q + 1], v);
     if (kRHT) rht16(v, a.rht_mask);
-    float srq[16];
-    if (kSR) sr_draws((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srq);
-    const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
+    uint32_t srr[16];
+    if (kSR) sr_operands((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srr);
+    const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
     store_block_stream(a.row_data, a.row_scales, 8 * b, b, c);
   }
 }
@@ -178,10 +178,10 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
       if (kRows && gr < R && gc < C) {
         float v[16];
         unpack16(w0, w1, v);
-        float srq[16];
+        uint32_t srr[16];
         const int64_t blk = gr * (C / 16) + gc / 16;
-        if (kSR) sr_draws((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srq);
-        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
+        if (kSR) sr_operands((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srr);
+        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
         rnib[row][4 * s + j] = make_uint2(c.lo, c.hi);
         rsc[row][4 * s + j] = (uint8_t)c.s;
       }
@@ -210,9 +210,9 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
         const int64_t col = gc + t2;
         if (kRHT) rht16(v, a.rht_mask);
         const int64_t blk = col * nrb + gr0 / 16;
-        float srq[16];
-        if (kSR) sr_draws((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srq);
-        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srq);
+        uint32_t srr[16];
+        if (kSR) sr_operands((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srr);
+        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
         store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
       }
     }
@@ -320,21 +320,21 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
     if (Rq >= R) break;                         // uniform across the workgroup
     float v[16];
     unpack16(w[2 * q], w[2 * q + 1], v);
-    float srq[16];
+    uint32_t srr[16];
     const int64_t rblk = (Rq + row) * tiles_c + T;    // row-wise block id of this row
-    if (kSR) sr_draws((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srq);
+    if (kSR) sr_operands((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srr);
 
     const float am = row16_max(amax16(v));
     Cand c6, c4;
     float inv6, inv4;
     cand_scale_bytes(am, tc.u6, tc.u4, c6.s, c4.s);
     cand_lookup(c6.s, tc.tab, c6.d, inv6);
-    if (kSR) cand_codes_sr(v, c6.d, inv6, srq, c6); else cand_codes_rne(v, c6.d, inv6, c6);
+    if (kSR) cand_codes_sr(v, c6.d, inv6, srr, c6); else cand_codes_rne(v, c6.d, inv6, c6);
     c6.err = row16_sum(c6.err);
     Cand c = c6;
     if (k46) {
       cand_lookup(c4.s, tc.tab, c4.d, inv4);
-      if (kSR) cand_codes_sr(v, c4.d, inv4, srq, c4); else cand_codes_rne(v, c4.d, inv4, c4);
+      if (kSR) cand_codes_sr(v, c4.d, inv4, srr, c4); else cand_codes_rne(v, c4.d, inv4, c4);
       c4.err = row16_sum(c4.err);
       if (c4.err < c6.err) c = c4;
     }

@@ -1,7 +1,7 @@
 // Device self-tests of the hardware conversions that the quantize kernels use in place
 // of the bit-level rules they stand for (format: Ultralytics glossary "FP4", opening
-// section and "How FP4 works"): fp32 -> E4M3 for the block scales and fp32 -> E2M1
-// for the element codes.  Each kernel runs every input of its range through both and
+// section and "How FP4 works"): fp32 -> E4M3 for the block scales, fp32 -> E2M1 for
+// the element codes, and fp32 -> E2M1 with stochastic rounding under the draws.  Each kernel runs every input of its range through both and
 // adds the number of disagreements to a device counter.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -58,6 +58,52 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_kernel(unsigned long l
   if (bad) atomicAdd(mismatches, (unsigned long long)bad);
 }
 
+// Self-test of the hardware stochastic rounding to E2M1 as the quantize kernels drive
+// it (operands from sr_operand, conversion by cvt_sr_fp4) against the draw rule: with
+// lo and hi the grid values around |v| and p = (|v| - lo) / (hi - lo), the code is
+// hi's iff (k + 0.5) / 256 < p; the sign of v is kept; 6 and above give 6.  The rule's
+// grid position is found here with plain comparisons (steps 0.5 below 2, 1 below 4,
+// 2 above), and p = y - floor(y) with y = |v| / step, both exact.  Every finite fp32
+// pattern is checked against all 256 draws, with -v as the other value of the pair;
+// each lane adds a nonzero disagreement count to *mismatches.
+__global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_kernel(unsigned long long* mismatches) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint32_t bad = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < ((uint64_t)1 << 32);
+       i += stride) {
+    const uint32_t b = (uint32_t)i;
+    if ((b & 0x7f800000u) == 0x7f800000u) continue;   // NaN, Inf
+    const float v = __uint_as_float(b);
+    const float m = fabsf(v);
+    const uint32_t sign = (b >> 31) << 3;
+    uint32_t lo_code, hi_code;
+    float p;
+    if (m >= 6.0f) {
+      lo_code = hi_code = 7u;
+      p = 0.0f;
+    } else {
+      const float step = (m < 2.0f) ? 0.5f : (m < 4.0f) ? 1.0f : 2.0f;
+      const float y = m / step;
+      const float yl = floorf(y);
+      p = y - yl;
+      // grid value yl * step -> its code: 2 * value below 2, then 4 (2), 5 (3), 6 (4)
+      lo_code = (m < 2.0f) ? (uint32_t)yl : (m < 4.0f) ? 2u + (uint32_t)yl : 6u;
+      hi_code = lo_code + 1u;
+    }
+    for (uint32_t k0 = 0; k0 < 256; k0 += 4) {
+      const uint32_t nw = ~(k0 * 0x01010101u + 0x03020100u);   // bytes k0 .. k0 + 3
+      uint32_t hw, expect;
+#define FOS_SR_CASE(B)                                                                   \
+      expect = (((float)(k0 + B) + 0.5f) * 0x1p-8f < p ? hi_code : lo_code) | sign;      \
+      hw = cvt_sr_fp4(v, -v, sr_operand<B>(nw)) & 0xfu;                                  \
+      bad += hw != expect;
+      FOS_SR_CASE(0) FOS_SR_CASE(1) FOS_SR_CASE(2) FOS_SR_CASE(3)
+#undef FOS_SR_CASE
+    }
+  }
+  if (bad) atomicAdd(mismatches, (unsigned long long)bad);
+}
+
 }  // namespace
 
 hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t s) {
@@ -67,6 +113,11 @@ hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t s) {
 
 hipError_t launch_selftest_e2m1(unsigned long long* mismatches, hipStream_t s) {
   selftest_e2m1_kernel<<<8192, kThreads, 0, s>>>(mismatches);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_e2m1_sr(unsigned long long* mismatches, hipStream_t s) {
+  selftest_e2m1_sr_kernel<<<8192, kThreads, 0, s>>>(mismatches);
   return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ def _load() -> ctypes.CDLL:
         "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "fos_selftest_e4m3": ([P, P], ctypes.c_int),
         "fos_selftest_e2m1": ([P, P], ctypes.c_int),
+        "fos_selftest_e2m1_sr": ([P, P], ctypes.c_int),
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_dequantize_hadamard": ([P, P, P, I64, I64, ctypes.c_uint64, ctypes.c_int, P, P],
                                     ctypes.c_int),
@@ -173,6 +174,15 @@ def selftest_e2m1(device="cuda:0") -> int:
     device."""
     n = torch.zeros(1, dtype=torch.int64, device=device)
     _check(_lib.fos_selftest_e2m1(_ptr(n), _stream(n.device)), "fos_selftest_e2m1")
+    return int(n.item())
+
+
+def selftest_e2m1_sr(device="cuda:0") -> int:
+    """Number of (finite fp32 value, draw byte) cases where the hardware stochastic
+    rounding to E2M1, under the operands the quantize kernels build from their draws,
+    differs from the draw rule; 0 on a correct device."""
+    n = torch.zeros(1, dtype=torch.int64, device=device)
+    _check(_lib.fos_selftest_e2m1_sr(_ptr(n), _stream(n.device)), "fos_selftest_e2m1_sr")
     return int(n.item())
 
 

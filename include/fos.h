@@ -164,6 +164,19 @@ fos_status fos_selftest_e4m3(unsigned long long* mismatches, void* stream);
  * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
 fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream);
 
+/* Self-test of the hardware stochastic rounding to E2M1 that the quantize kernels use
+ * with FOS_ROUND_SR (gfx950's fp32 -> FP4 conversion with a 32-bit rounding operand,
+ * scale 1), driven exactly as the kernels drive it (the operand built from the draw
+ * byte and the value's low pattern bits): for every finite fp32 value v and every draw
+ * byte k in 0..255, the code must be the draw rule's -- with lo and hi the E2M1 values
+ * around min(|v|, 6) and p = (|v| - lo) / (hi - lo), hi iff (k + 0.5) / 256 < p, with
+ * the sign of v (the stochastic rounding of the Four Over Six page, section "Four
+ * Over Six", under the draws this library takes).  Adds to *mismatches (device
+ * uint64, 8-byte aligned; the caller zeroes it) the number of disagreements over
+ * those 256 x (2^32 - 2^24) cases.  A correct device gives 0.  Takes under a second.
+ * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_selftest_e2m1_sr(unsigned long long* mismatches, void* stream);
+
 /* Dequantize one NVFP4 record: out[r][c] = RN_fp32(E2M1(q) * RN_fp32(E4M3(s) * t))
  * with the nibble's sign (-0 for code 8); FOS_OUT_BF16 rounds that fp32 value to
  * bf16 (nearest-even).  Works for row-wise, column-wise (giving X^T) and 2D records.

@@ -157,6 +157,8 @@ def test_selftest_validation():
     assert L.fos_selftest_e4m3(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
     assert L.fos_selftest_e2m1(None, None) == fos.FOS_E_NULL
     assert L.fos_selftest_e2m1(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
+    assert L.fos_selftest_e2m1_sr(None, None) == fos.FOS_E_NULL
+    assert L.fos_selftest_e2m1_sr(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
 
 
 def test_qlinear_act_validation():

@@ -149,6 +149,14 @@ def test_hardware_e2m1_conversion_matches_rule(fos):
     assert fos.selftest_e2m1() == 0
 
 
+def test_hardware_e2m1_stochastic_rounding_matches_rule(fos):
+    """With stochastic rounding the quantize kernels round element values with the
+    hardware conversion under an operand built from each draw byte k; on every finite
+    fp32 value and every k it must give the draw rule's code (up iff (k + 0.5)/256 < p,
+    sign kept, 6 and above give 6) that the oracle implements."""
+    assert fos.selftest_e2m1_sr() == 0
+
+
 @pytest.mark.parametrize("rows", [1, 3, 7])
 def test_row_wise_any_row_count(fos, rows):
     bits = bits_of(W.random_bf16(rows, 4096 + 48, 55 + rows, "student_t"))
