@@ -56,7 +56,7 @@ hipError_t launch_selftest_e2m1(unsigned long long* mismatches, hipStream_t stre
 
 // Adds to *mismatches the number of disagreements between the hardware stochastic
 // rounding to E2M1 under the operands the quantize kernels build from their draws and
-// the draw rule, over every finite fp32 and every draw byte.
+// the draw rule, over every finite fp32 and every draw byte, at both pair positions.
 hipError_t launch_selftest_e2m1_sr(unsigned long long* mismatches, hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,

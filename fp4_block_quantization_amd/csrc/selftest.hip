@@ -59,13 +59,14 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_kernel(unsigned long l
 }
 
 // Self-test of the hardware stochastic rounding to E2M1 as the quantize kernels drive
-// it (operands from sr_operand, conversion by cvt_sr_fp4) against the draw rule: with
+// it (operands from sr_operand, conversion by cvt_sr_fp4_first and cvt_sr_fp4_second)
+// against the draw rule: with
 // lo and hi the grid values around |v| and p = (|v| - lo) / (hi - lo), the code is
 // hi's iff (k + 0.5) / 256 < p; the sign of v is kept; 6 and above give 6.  The rule's
 // grid position is found here with plain comparisons (steps 0.5 below 2, 1 below 4,
 // 2 above), and p = y - floor(y) with y = |v| / step, both exact.  Every finite fp32
-// pattern is checked against all 256 draws, with -v as the other value of the pair;
-// each lane adds a nonzero disagreement count to *mismatches.
+// pattern is checked against all 256 draws, at both positions of a pair (with -v as
+// the other value); each lane adds a nonzero disagreement count to *mismatches.
 __global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_kernel(unsigned long long* mismatches) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   uint32_t bad = 0;
@@ -92,11 +93,13 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_kernel(unsigned lon
     }
     for (uint32_t k0 = 0; k0 < 256; k0 += 4) {
       const uint32_t nw = ~(k0 * 0x01010101u + 0x03020100u);   // bytes k0 .. k0 + 3
-      uint32_t hw, expect;
+      uint32_t r, hw1, hw2, expect;
 #define FOS_SR_CASE(B)                                                                   \
       expect = (((float)(k0 + B) + 0.5f) * 0x1p-8f < p ? hi_code : lo_code) | sign;      \
-      hw = cvt_sr_fp4(v, -v, sr_operand<B>(nw)) & 0xfu;                                  \
-      bad += hw != expect;
+      r = sr_operand<B>(nw);                                                             \
+      hw1 = cvt_sr_fp4_first(f32x2{v, -v}, r) & 0xfu;                                    \
+      hw2 = (cvt_sr_fp4_second(f32x2{-v, v}, r) >> 4) & 0xfu;                            \
+      bad += (hw1 != expect) + (hw2 != expect);
       FOS_SR_CASE(0) FOS_SR_CASE(1) FOS_SR_CASE(2) FOS_SR_CASE(3)
 #undef FOS_SR_CASE
     }

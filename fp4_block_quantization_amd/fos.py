@@ -178,9 +178,9 @@ def selftest_e2m1(device="cuda:0") -> int:
 
 
 def selftest_e2m1_sr(device="cuda:0") -> int:
-    """Number of (finite fp32 value, draw byte) cases where the hardware stochastic
-    rounding to E2M1, under the operands the quantize kernels build from their draws,
-    differs from the draw rule; 0 on a correct device."""
+    """Number of (finite fp32 value, draw byte, pair position) cases where the
+    hardware stochastic rounding to E2M1, under the operands the quantize kernels
+    build from their draws, differs from the draw rule; 0 on a correct device."""
     n = torch.zeros(1, dtype=torch.int64, device=device)
     _check(_lib.fos_selftest_e2m1_sr(_ptr(n), _stream(n.device)), "fos_selftest_e2m1_sr")
     return int(n.item())

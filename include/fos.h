@@ -171,9 +171,10 @@ fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream);
  * byte k in 0..255, the code must be the draw rule's -- with lo and hi the E2M1 values
  * around min(|v|, 6) and p = (|v| - lo) / (hi - lo), hi iff (k + 0.5) / 256 < p, with
  * the sign of v (the stochastic rounding of the Four Over Six page, section "Four
- * Over Six", under the draws this library takes).  Adds to *mismatches (device
- * uint64, 8-byte aligned; the caller zeroes it) the number of disagreements over
- * those 256 x (2^32 - 2^24) cases.  A correct device gives 0.  Takes under a second.
+ * Over Six", under the draws this library takes), at both positions of a pair.
+ * Adds to *mismatches (device uint64, 8-byte aligned; the caller zeroes it) the number
+ * of disagreements over those 2 x 256 x (2^32 - 2^24) cases.  A correct device gives
+ * 0.  Takes about a second.
  * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
 fos_status fos_selftest_e2m1_sr(unsigned long long* mismatches, void* stream);
 
