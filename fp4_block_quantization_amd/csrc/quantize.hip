@@ -6,8 +6,8 @@
 // Three kernels, all one-pass over the bf16 input with every 16-value block held in
 // one lane's registers while both candidates are evaluated:
 //   quant_rows_kernel  row-wise 1D output: the tensor is a flat run of 16-value
-//                      blocks; lane = two blocks; two 16-byte loads, one 8-byte store
-//                      of nibbles and one scale byte per block.
+//                      blocks; lane = one block; two 16-byte loads, one 8-byte store
+//                      of nibbles and one scale byte.
 //   quant_tile_kernel  column-wise output (optionally row-wise from the same read):
 //                      a 128x64 tile goes through LDS (XOR-swizzled 16-byte groups,
 //                      so the column reads spread over the banks); each lane then
@@ -66,44 +66,36 @@ __device__ __forceinline__ void store_block(uint8_t* data, uint8_t* scales, int6
 // store_block_stream instead.)
 
 // ------------------------------------------------------------------ row-wise, 1D
-// Each lane owns blocks b and b + 256 of its workgroup's 512; both blocks' four
-// 16-byte loads are issued before either is quantized.
-constexpr int kRowsPerWG = 2 * kThreads;
+// One block per lane: a workgroup covers 256 consecutive blocks, each lane issues its
+// block's two 16-byte loads before the workgroup's set-up and quantizes it from
+// registers.  With one block per lane the Hadamard + stochastic-rounding variant needs
+// 61 VGPRs (8 waves per SIMD) instead of the 92 (5 waves) of two blocks per lane; that
+// variant is bound by VALU issue and the extra waves hide its dependent chains.
+constexpr int kRowsPerWG = kThreads;
 
 template <bool k46, bool kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
-  const uint4* __restrict__ x = reinterpret_cast<const uint4*>(a.x);
-  const int64_t b0 = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
-  uint4 w[4];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t b = b0 + q * kThreads;
-    w[2 * q] = make_uint4(0, 0, 0, 0);
-    w[2 * q + 1] = w[2 * q];
-    if (b < nblk) {
-      // input read once: non-temporal loads
-      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-      const v4u* xv = reinterpret_cast<const v4u*>(x);
-      const v4u l0 = __builtin_nontemporal_load(xv + 2 * b);
-      const v4u l1 = __builtin_nontemporal_load(xv + 2 * b + 1);
-      w[2 * q] = make_uint4(l0.x, l0.y, l0.z, l0.w);
-      w[2 * q + 1] = make_uint4(l1.x, l1.y, l1.z, l1.w);
-    }
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const int64_t b = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
+  uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+  if (b < nblk) {
+    // input read once: non-temporal loads
+    const v4u* xv = reinterpret_cast<const v4u*>(a.x);
+    const v4u l0 = __builtin_nontemporal_load(xv + 2 * b);
+    const v4u l1 = __builtin_nontemporal_load(xv + 2 * b + 1);
+    w0 = make_uint4(l0.x, l0.y, l0.z, l0.w);
+    w1 = make_uint4(l1.x, l1.y, l1.z, l1.w);
   }
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t b = b0 + q * kThreads;
-    if (b >= nblk) break;
-    float v[16];
-    unpack16(w[2 * q], w[2 * q + 1], v);
-    if (kRHT) rht16(v, a.rht_mask);
-    uint32_t srr[16];
-    if (kSR) sr_operands((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srr);
-    const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
-    store_block_stream(a.row_data, a.row_scales, 8 * b, b, c);
-  }
+  if (b >= nblk) return;
+  float v[16];
+  unpack16(w0, w1, v);
+  if (kRHT) rht16(v, a.rht_mask);
+  uint32_t srr[16];
+  if (kSR) sr_operands((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srr);
+  const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
+  store_block_stream(a.row_data, a.row_scales, 8 * b, b, c);
 }
 
 // ------------------------------------------------------------------ column-wise tiles
