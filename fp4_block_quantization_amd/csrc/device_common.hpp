@@ -137,14 +137,19 @@ __device__ __forceinline__ f32x2 cvt_pk_f32_fp4(uint32_t w) {
 }
 
 // ---- Philox4x32-10 (Salmon et al., SC'11) ----------------------------------------
+// Three-input exclusive or in one instruction (v_bitop3_b32 with truth table 0x96:
+// the result bit is set where an odd number of the three input bits are).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
-                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1,
+                   xor3((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0);
   }
   return c;
 }
@@ -233,20 +238,29 @@ __device__ __forceinline__ void fwht16(float (&y)[16]) {
   }
 }
 
+// Sign bit k of the transform (bit k of `mask`) at bit 31.  The mask is the same for
+// every lane, so these are scalar operations and each sign reaches the vector
+// instruction as a scalar operand.
+__device__ __forceinline__ uint32_t rht_sign_bit(uint32_t mask, int k) {
+  return ((mask >> k) & 1u) << 31;
+}
+
 // Forward transform: y_k = x_k * (+-1/4) (sign k from bit k of `mask`), then H16.
+// The factor +-1/4 is the fp32 pattern of 1/4 (0x3e800000) with the sign bit set.
 __device__ __forceinline__ void rht16(float (&y)[16], uint32_t mask) {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) y[k] *= ((mask >> k) & 1u) ? -0.25f : 0.25f;
+  for (int k = 0; k < 16; ++k) y[k] *= __uint_as_float(0x3e800000u | rht_sign_bit(mask, k));
   fwht16(y);
 }
 
-// Inverse transform ((H/4)^-1 = H/4, S^-1 = S): y_k *= 1/4, then H16, then the signs.
+// Inverse transform ((H/4)^-1 = H/4, S^-1 = S): y_k *= 1/4, then H16, then the signs
+// (a sign flip of the fp32 pattern).
 __device__ __forceinline__ void irht16(float (&y)[16], uint32_t mask) {
 #pragma unroll
   for (int k = 0; k < 16; ++k) y[k] *= 0.25f;
   fwht16(y);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) y[k] = ((mask >> k) & 1u) ? -y[k] : y[k];
+  for (int k = 0; k < 16; ++k) y[k] = __uint_as_float(__float_as_uint(y[k]) ^ rht_sign_bit(mask, k));
 }
 
 // ---- one candidate scale for one 16-value block ------------------------------------
