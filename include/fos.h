@@ -167,11 +167,12 @@ fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream);
 /* Self-test of the hardware stochastic rounding to E2M1 that the quantize kernels use
  * with FOS_ROUND_SR (gfx950's fp32 -> FP4 conversion with a 32-bit rounding operand,
  * scale 1), driven exactly as the kernels drive it (the operand built from the draw
- * byte and the value's low pattern bits): for every finite fp32 value v and every draw
- * byte k in 0..255, the code must be the draw rule's -- with lo and hi the E2M1 values
- * around min(|v|, 6) and p = (|v| - lo) / (hi - lo), hi iff (k + 0.5) / 256 < p, with
- * the sign of v (the stochastic rounding of the Four Over Six page, section "Four
- * Over Six", under the draws this library takes), at both positions of a pair.
+ * byte): for every finite fp32 value v and every draw byte k in 0..255, the code must
+ * be the draw rule's -- with lo and hi the E2M1 values around min(|v|, 6),
+ * p = (|v| - lo) / (hi - lo) and p22 = p truncated to 22 fractional bits, hi iff
+ * (k + 0.5) / 256 < p22, with the sign of v (the stochastic rounding of the Four Over
+ * Six page, section "Four Over Six", under the draws this library takes), at both
+ * positions of a pair.
  * Adds to *mismatches (device uint64, 8-byte aligned; the caller zeroes it) the number
  * of disagreements over those 2 x 256 x (2^32 - 2^24) cases.  A correct device gives
  * 0.  Takes about a second.

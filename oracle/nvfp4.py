@@ -45,8 +45,9 @@ kept; "RN(.)" is one fp32 rounding):
       (stream 0 row-wise, 1 column-wise); element i takes byte i of the 16 output
       bytes (byte (i % 4) of word i // 4), call it k in 0..255.  For |v| >= 6 the code
       is 6.  Otherwise lo/hi are the grid values around |v|, p = (|v| - lo)/(hi - lo)
-      (exact), and the value rounds up to hi iff (k + 0.5)/256 < p.  Both candidates
-      use the same draws and the choice compares the errors of the rounded values.
+      (exact), p22 = p truncated to 22 fractional bits, and the value rounds up to hi
+      iff (k + 0.5)/256 < p22.  Both candidates use the same draws and the choice
+      compares the errors of the rounded values.
       2D tiles take the draws of the row-wise layout for every output.
 
 The element-wise scale uses a per-block reciprocal and the per-block scale uses a
@@ -107,7 +108,12 @@ def sr_bytes(block_ids: np.ndarray, seed: int, stream: int) -> np.ndarray:
 
 
 def e2m1_sr_code(magnitude: np.ndarray, k: np.ndarray) -> np.ndarray:
-    """Stochastic rounding of |v| >= 0 onto the E2M1 grid with draw k in 0..255."""
+    """Stochastic rounding of |v| >= 0 onto the E2M1 grid with draw k in 0..255.
+
+    The position p of |v| between its grid neighbours is exact in fp64 (the grid steps
+    are powers of two) and is truncated to 22 fractional bits before it is compared
+    with the draw's threshold (k + 0.5)/256; the truncation moves the probability of
+    rounding up by less than 2^-22."""
     m = np.asarray(magnitude, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     lo = np.searchsorted(E2M1_GRID, m, side="right") - 1     # grid[lo] <= m
@@ -115,7 +121,8 @@ def e2m1_sr_code(magnitude: np.ndarray, k: np.ndarray) -> np.ndarray:
     hi = np.minimum(lo + 1, 7)
     step = E2M1_GRID[hi] - E2M1_GRID[lo]
     p = np.where(step > 0, (m - E2M1_GRID[lo]) / np.where(step > 0, step, 1.0), 0.0)
-    up = ((k + 0.5) / 256.0) < p
+    p22 = np.floor(p * 2.0 ** 22) / 2.0 ** 22
+    up = ((k + 0.5) / 256.0) < p22
     code = np.where(up, hi, lo)
     code = np.where(m >= 6.0, 7, code)
     return code.astype(np.uint8)

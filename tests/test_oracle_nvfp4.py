@@ -282,9 +282,32 @@ def test_sr_keeps_grid_values_and_is_unbiased():
         lo = grid[grid <= v].max()
         hi = grid[grid > v].min() if v < 6 else 6.0
         assert set(np.unique(out)) <= {lo, hi}
-        # exhaustive over the 256 draws: mean within 1/512 of a grid step of v
-        assert abs(out.mean() - v) <= (hi - lo) / 512 + 1e-12
+        # exhaustive over the 256 draws: mean within 1/512 (the draws' resolution) plus
+        # 2^-22 (the position's truncation) of a grid step of v
+        assert abs(out.mean() - v) <= (hi - lo) * (1 / 512 + 2.0 ** -22) + 1e-12
     assert np.all(grid[N.e2m1_sr_code(np.array([6.0, 7.0, 100.0]), np.array([0, 128, 255]))] == 6)
+
+
+def test_sr_position_is_truncated_to_22_fraction_bits():
+    """Worked by hand: on [0.5, 1) the grid step is 0.5, so p = 2 (|v| - 0.5), and draw
+    k = 0 has threshold q = 0.5/256 = 2^-9.  |v| = 0.5 + 2^-10 gives p = q exactly (no
+    rounding up: the comparison is strict); one fp32 ulp (2^-24) above it p exceeds q by
+    2^-23, which the truncation to 22 fractional bits drops (down); two ulps above, by
+    2^-22, which it keeps (up).  Below 0.5 (step 0.5, lo = 0) the same holds at
+    |v| = 2^-10 + 2^-30 (down) and 2^-10 + 2^-23 (up).  On [2, 4) (step 1, exact p) the
+    threshold of k = 255 is 1 - 2^-9: |v| = 3 - 2^-9 stays at 2, the next fp32 value up
+    rounds to 3."""
+    grid = F.E2M1_GRID
+    def up(v, k):
+        c = N.e2m1_sr_code(np.array([np.float32(v)], dtype=np.float64), np.array([k]))[0]
+        return grid[c] > v
+    assert not up(0.5 + 2.0 ** -10, 0)
+    assert not up(0.5 + 2.0 ** -10 + 2.0 ** -24, 0)
+    assert up(0.5 + 2.0 ** -10 + 2.0 ** -23, 0)
+    assert not up(2.0 ** -10 + 2.0 ** -30, 0)
+    assert up(2.0 ** -10 + 2.0 ** -23, 0)
+    assert not up(3.0 - 2.0 ** -9, 255)
+    assert up(float(np.nextafter(np.float32(3.0 - 2.0 ** -9), np.float32(4.0))), 255)
 
 
 def test_sr_tensor_mean_close_to_input():
