@@ -191,24 +191,32 @@ __device__ __forceinline__ void sr_operands(uint64_t block, uint32_t stream, uin
     r[4 * m + 3] = sr_operand<3>(nw[m]) >> 1;
   }
 }
-// Stochastic codes of the pair v = (v0, v1): cvt_sr_fp4_first under v0's operand gives
-// v0's code in the low nibble of byte 0, cvt_sr_fp4_second under v1's (shifted)
-// operand gives v1's code in the high nibble of byte 0.  Every other bit of either
-// result is unspecified: the instruction leaves bytes 1..3 of its destination register
-// as they were, and the compiler does not load the builtin's `old` operand into that
-// register.  Scale operand 1.0 = no scaling.
-__device__ __forceinline__ uint32_t cvt_sr_fp4_first(f32x2 v, uint32_t r0) {
-  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, r0, 1.0f, 0);
+// Stochastic codes of the pair v = (v0, v1) into byte SEL of `w`, the other three bytes
+// of `w` kept: under v0's operand the byte's low nibble is v0's code, under v1's
+// (shifted) operand its high nibble is v1's code; the other nibble of the byte is then
+// unspecified.  Scale operand 1.0 = no scaling.  The compiler's builtin for this
+// instruction does not tie its `old` operand to the destination register, so the
+// bytes it should keep are lost; a read-write inline-assembly operand keeps them (the
+// instruction only reads and writes registers).
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_sr_fp4_byte(uint32_t w, f32x2 v, uint32_t r) {
+  static_assert(SEL >= 0 && SEL < 4, "byte select");
+  if constexpr (SEL == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(v), "v"(r));
+  else if constexpr (SEL == 1)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(w) : "v"(v), "v"(r));
+  else if constexpr (SEL == 2)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(w) : "v"(v), "v"(r));
+  else
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(w) : "v"(v), "v"(r));
+  return w;
 }
-__device__ __forceinline__ uint32_t cvt_sr_fp4_second(f32x2 v, uint32_t r1) {
-  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, r1, 1.0f, 0);
-}
-// Byte 0 of w0, w1, w2, w3 -> bytes 0, 1, 2, 3 of the result.
-__device__ __forceinline__ uint32_t gather_byte0(uint32_t w0, uint32_t w1, uint32_t w2,
-                                                 uint32_t w3) {
-  const uint32_t t01 = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);
-  const uint32_t t23 = __builtin_amdgcn_perm(w3, w2, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+// A register the code words start from: every byte is written before it is read, so
+// its value does not matter and no instruction sets it.
+__device__ __forceinline__ uint32_t any_word() {
+  uint32_t w;
+  asm("" : "=v"(w));
+  return w;
 }
 
 // ---- random-sign 16-point Hadamard transform ---------------------------------------
@@ -337,21 +345,22 @@ __device__ __forceinline__ void cand_codes_rne(const float (&x)[16], float d, fl
 
 // Stochastic-rounding codes (hardware conversion under the draws' operands, see above)
 // and the sequential squared error of the decoded values.  Each pair of elements is
-// converted twice, once for each of its codes; the codes are gathered byte by byte
-// and merged nibble by nibble.
+// converted twice, once for each of its codes, into the byte of its pair; the two
+// words of a half-block are merged nibble by nibble.
 __device__ __forceinline__ void cand_codes_sr(const float (&x)[16], float d, float inv,
                                               const uint32_t (&r)[16], Cand& c) {
-  uint32_t ev[8], od[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const f32x2 v = {x[2 * j] * inv, x[2 * j + 1] * inv};
-    ev[j] = cvt_sr_fp4_first(v, r[2 * j]);
-    od[j] = cvt_sr_fp4_second(v, r[2 * j + 1]);
+  // e*: byte j holds pair j's conversion under the even element's operand (low nibble
+  // valid); o*: under the odd element's (high nibble valid); then one merge per word.
+  uint32_t e0 = any_word(), o0 = any_word(), e1 = any_word(), o1 = any_word();
+#define FOS_SR_PAIR(J, E, O)                                                          \
+  {                                                                                   \
+    const f32x2 v = {x[2 * (J)] * inv, x[2 * (J) + 1] * inv};                         \
+    E = cvt_sr_fp4_byte<(J) & 3>(E, v, r[2 * (J)]);                                   \
+    O = cvt_sr_fp4_byte<(J) & 3>(O, v, r[2 * (J) + 1]);                               \
   }
-  const uint32_t e0 = gather_byte0(ev[0], ev[1], ev[2], ev[3]);
-  const uint32_t o0 = gather_byte0(od[0], od[1], od[2], od[3]);
-  const uint32_t e1 = gather_byte0(ev[4], ev[5], ev[6], ev[7]);
-  const uint32_t o1 = gather_byte0(od[4], od[5], od[6], od[7]);
+  FOS_SR_PAIR(0, e0, o0) FOS_SR_PAIR(1, e0, o0) FOS_SR_PAIR(2, e0, o0) FOS_SR_PAIR(3, e0, o0)
+  FOS_SR_PAIR(4, e1, o1) FOS_SR_PAIR(5, e1, o1) FOS_SR_PAIR(6, e1, o1) FOS_SR_PAIR(7, e1, o1)
+#undef FOS_SR_PAIR
   const uint32_t lo = (e0 & 0x0f0f0f0fu) | (o0 & 0xf0f0f0f0u);
   const uint32_t hi = (e1 & 0x0f0f0f0fu) | (o1 & 0xf0f0f0f0u);
   f32x2 e[8];

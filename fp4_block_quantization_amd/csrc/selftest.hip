@@ -60,10 +60,10 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_kernel(unsigned long l
 
 // Self-test of the hardware stochastic rounding to E2M1 as the quantize kernels drive
 // it (operands from sr_operand, the second position's shifted right by one; conversion
-// by cvt_sr_fp4_first and cvt_sr_fp4_second) against the draw rule: with lo and hi the
-// grid values around |v|, p = (|v| - lo) / (hi - lo) and p22 = p truncated to 22
-// fractional bits, the code is hi's iff (k + 0.5) / 256 < p22; the sign of v is kept;
-// 6 and above give 6.  The rule's grid position is found here with plain comparisons
+// by cvt_sr_fp4_byte into each of the four bytes of a word, the other bytes kept)
+// against the draw rule: with lo and hi the grid values around |v|,
+// p = (|v| - lo) / (hi - lo) and p22 = p truncated to 22 fractional bits, the code is
+// hi's iff (k + 0.5) / 256 < p22; the sign of v is kept; 6 and above give 6.  The rule's grid position is found here with plain comparisons
 // (steps 0.5 below 2, 1 below 4, 2 above), and p = y - floor(y) with y = |v| / step,
 // both exact, as is p22 = floor(p * 2^22) * 2^-22.  Every finite fp32 pattern is
 // checked against all 256 draws, at both positions of a pair (with -v as the other
@@ -94,15 +94,18 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_kernel(unsigned lon
     }
     for (uint32_t k0 = 0; k0 < 256; k0 += 4) {
       const uint32_t nw = ~(k0 * 0x01010101u + 0x03020100u);   // bytes k0 .. k0 + 3
-      uint32_t r, hw1, hw2, expect;
+      // draw k0 + B goes to byte B of both words (first position in w1, second in w2)
+      uint32_t w1 = any_word(), w2 = any_word(), expect[4], r;
 #define FOS_SR_CASE(B)                                                                   \
-      expect = (((float)(k0 + B) + 0.5f) * 0x1p-8f < p ? hi_code : lo_code) | sign;      \
+      expect[B] = (((float)(k0 + B) + 0.5f) * 0x1p-8f < p ? hi_code : lo_code) | sign;   \
       r = sr_operand<B>(nw);                                                             \
-      hw1 = cvt_sr_fp4_first(f32x2{v, -v}, r) & 0xfu;                                    \
-      hw2 = (cvt_sr_fp4_second(f32x2{-v, v}, r >> 1) >> 4) & 0xfu;                       \
-      bad += (hw1 != expect) + (hw2 != expect);
+      w1 = cvt_sr_fp4_byte<B>(w1, f32x2{v, -v}, r);                                      \
+      w2 = cvt_sr_fp4_byte<B>(w2, f32x2{-v, v}, r >> 1);
       FOS_SR_CASE(0) FOS_SR_CASE(1) FOS_SR_CASE(2) FOS_SR_CASE(3)
 #undef FOS_SR_CASE
+#pragma unroll
+      for (int B = 0; B < 4; ++B)
+        bad += (((w1 >> (8 * B)) & 0xfu) != expect[B]) + (((w2 >> (8 * B + 4)) & 0xfu) != expect[B]);
     }
   }
   if (bad) atomicAdd(mismatches, (unsigned long long)bad);
