@@ -177,8 +177,9 @@ def _candidate(x: np.ndarray, a: np.ndarray, t: F32, c: float,
     for j in range(16):
         rows = fma32(e[:, :, j], e[:, :, j], rows)
     level = rows
-    while level.shape[1] > 1:                               # pairwise over rows
-        level = (level[:, 0::2] + level[:, 1::2]).astype(F32)
+    with np.errstate(over="ignore"):                        # huge blocks: fp32 sums overflow to inf
+        while level.shape[1] > 1:                           # pairwise over rows
+            level = (level[:, 0::2] + level[:, 1::2]).astype(F32)
     return S, m, level[:, 0]
 
 
