@@ -88,6 +88,9 @@ def test_launch_grid_limit():
     f = FAKE
     # 2D tiles: (2^25 - 1) tile rows / 2 per workgroup -> 2^24 workgroups of 256
     assert q(cfg(block="2d"), rows=(1 << 29) - 16, cols=16) == fos.FOS_E_SHAPE
+    # row-wise, one 16-value block per lane: 2^26 x 1040 -> 4,362,076,160 blocks in
+    # 17,039,360 workgroups of 256 (more than (2^32 - 1) / 256)
+    assert q(cfg(), rows=1 << 26, cols=1040) == fos.FOS_E_SHAPE
     # column-wise 128 x 64 tiles of a [2^31 - 16, 16] tensor -> 2^24 workgroups
     assert q(cfg(outputs=("col",)), rows=(1 << 31) - 16, cols=16) == fos.FOS_E_SHAPE
     t = ctypes.byref(cfg(outputs=("col",)))
