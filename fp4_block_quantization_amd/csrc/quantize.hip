@@ -256,11 +256,19 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
-  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+// Maximum of non-negative values, taken on their bit patterns (for non-negative floats
+// the unsigned order is the value order): one max with a DPP operand per step, where a
+// float max would also quiet a possible NaN in the permuted copy.
+__device__ __forceinline__ float row16_max(float f) {
+  uint32_t v = __float_as_uint(f);
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));   // row_half_mirror
+  return __uint_as_float(max(v, dpp_u32<0x140>(v)));  // row_mirror
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v = v + dpp_f32<0xB1>(v);
