@@ -197,6 +197,8 @@ const char* fos_status_string(fos_status s) {
   return "FOS_E_UNKNOWN";
 }
 
+size_t fos_quantize_workspace_bytes(void) { return kWorkspaceBytes; }
+
 size_t fos_workspace_bytes(void) { return kWorkspaceBytes; }
 
 fos_status fos_tensor_scale(const fos_quant_config* cfg, const void* x, int64_t rows,

@@ -50,6 +50,7 @@ def _load() -> ctypes.CDLL:
     sigs = {
         "fos_abi_version": ([], ctypes.c_int),
         "fos_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "fos_quantize_workspace_bytes": ([], SZ),
         "fos_workspace_bytes": ([], SZ),
         "fos_tensor_scale": ([cfgp, P, I64, I64, P, P, SZ, P], ctypes.c_int),
         "fos_quantize_scaled": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
@@ -126,7 +127,7 @@ def workspace(device: torch.device) -> torch.Tensor:
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None:
-        ws = torch.zeros(int(_lib.fos_workspace_bytes()), dtype=torch.uint8, device=device)
+        ws = torch.zeros(int(_lib.fos_quantize_workspace_bytes()), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

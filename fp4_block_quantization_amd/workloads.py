@@ -27,6 +27,7 @@ from __future__ import annotations
 import torch
 
 __all__ = [
+    "normal_with_outliers",
     "page_example",
     "make",
     "random_bf16",
@@ -45,12 +46,21 @@ SHAPES = {
 }
 
 
-def page_example() -> torch.Tensor:
-    """The worked example's input: 4096 N(0,1) fp32 values, every 512th times 20."""
-    torch.manual_seed(0)
-    x = torch.randn(4096)
-    x[::512] *= 20
+def normal_with_outliers(shape, seed: int = 0, every: int = 512,
+                         factor: float = 20.0) -> torch.Tensor:
+    """fp32 N(0,1) values from torch's global generator seeded with ``seed``, with
+    every ``every``-th value of the flat tensor multiplied by ``factor`` (in fp32).
+    The worked example of the Ultralytics glossary page "FP4" (§How FP4 works) draws
+    its tensor this way with seed 0, every 512th value, factor 20."""
+    torch.manual_seed(seed)
+    x = torch.randn(*shape)
+    x.view(-1)[::every] *= factor
     return x
+
+
+def page_example() -> torch.Tensor:
+    """The worked example's input: 4096 fp32 values of ``normal_with_outliers``."""
+    return normal_with_outliers((4096,))
 
 
 def _student_t(shape, seed: int, scale: float) -> torch.Tensor:
@@ -63,9 +73,7 @@ def make(name: str) -> torch.Tensor:
     """Return the named workload as a contiguous CPU bfloat16 tensor."""
     shape = SHAPES[name]
     if name == "c1":
-        torch.manual_seed(0)
-        x = torch.randn(*shape)
-        x.view(-1)[::512] *= 20
+        x = normal_with_outliers(shape)
     elif name == "c2":
         g = torch.Generator().manual_seed(2)
         x = 0.02 * torch.randn(*shape, generator=g)

@@ -71,7 +71,11 @@ typedef enum {
 enum { FOS_RULE_4OVER6 = 0, FOS_RULE_6ONLY = 1 };
 /* E2M1 rounding: nearest-even, or stochastic (one Philox4x32-10 draw per block,
  * 8 random bits per element; the pages list stochastic rounding as an option and
- * the FP4 glossary's training section uses it for gradients). */
+ * the FP4 glossary's training section uses it for gradients).  With 8-bit draws a
+ * value at fractional position p between its two grid neighbours rounds up with
+ * chance n/256, n = number of draw bytes k with (k + 0.5)/256 < p (p taken to 22
+ * fractional bits): p <= 1/512 never rounds up, p > 511/512 always does, and the
+ * expected result is off by at most 2^-9 of the grid step (plus 2^-22). */
 enum { FOS_ROUND_RNE = 0, FOS_ROUND_STOCHASTIC = 1 };
 /* 1D: 16 consecutive values share a scale.  2D: a 16x16 tile shares one scale and
  * one 4-vs-6 decision; its byte is written into all 16 row-block slots of the tile
@@ -104,7 +108,12 @@ const char* fos_status_string(fos_status status);
 /* Bytes of device workspace that fos_tensor_scale / fos_quantize need (scratch for
  * the per-workgroup partial maxima of the tensor-scale pass, 16-byte aligned; its
  * contents on entry are ignored, and it must stay untouched until the call's
- * kernels have run). */
+ * kernels have run).  The per-tensor FP32 scale that the pass computes is the
+ * second-level scale of NVFP4 (Ultralytics glossary "FP4", "How FP4 works").
+ * The size does not depend on the tensor: 4096 bytes. */
+size_t fos_quantize_workspace_bytes(void);
+
+/* The same value as fos_quantize_workspace_bytes (earlier name, kept). */
 size_t fos_workspace_bytes(void);
 
 /* Per-tensor scale.  Writes t = RN_fp32(A / 2688) to *tensor_scale (device fp32),
@@ -124,6 +133,13 @@ fos_status fos_tensor_scale(const fos_quant_config* cfg, const void* x, int64_t 
 
 /* 4/6 quantization given the tensor scale (device fp32, e.g. from
  * fos_tensor_scale, or the all-reduced maximum of per-shard scales).
+ * Per 16-value block (Four Over Six documentation page, "Four Over Six"): the
+ * block's E4M3 scale maps its largest magnitude to 6 or to 4, the candidate with
+ * the lower squared error of the dequantized block is kept (ties go to 6;
+ * FOS_RULE_6ONLY keeps 6), and the values are rounded onto the E2M1 grid under it.
+ * The record is NVFP4's (Ultralytics glossary "FP4", "How FP4 works": 16 E2M1 values
+ * per E4M3 scale, one FP32 scale per tensor); the options (2D blocks, transposed
+ * output, Hadamard transform, stochastic rounding) are the page's list.
  *   row_data [rows][cols/2], row_scales [rows][cols/16]: required iff
  *     cfg->outputs has FOS_OUT_ROWWISE, else ignored.  row_data 8-byte aligned.
  *   col_data [cols][rows/2], col_scales [cols][rows/16]: required iff
@@ -135,9 +151,17 @@ fos_status fos_quantize_scaled(const fos_quant_config* cfg, const void* x, int64
                                uint8_t* row_data, uint8_t* row_scales,
                                uint8_t* col_data, uint8_t* col_scales, void* stream);
 
-/* fos_tensor_scale followed by fos_quantize_scaled on the same stream, with the same
+/* Four Over Six quantization of a bf16 tensor into an NVFP4 record (Four Over Six
+ * documentation page, "Four Over Six": per block, max -> 6 or max -> 4, whichever
+ * gives the lower error; Ultralytics glossary "FP4", "How FP4 works": 16 E2M1 values
+ * per E4M3 scale plus one FP32 tensor scale).
+ * fos_tensor_scale followed by fos_quantize_scaled on the same stream, with the same
  * results; the tensor scale is written to *tensor_scale.  (The partial maxima of the
- * scale pass are reduced inside the quantize kernel, which saves one launch.) */
+ * scale pass are reduced inside the quantize kernel, which saves one launch.)
+ *   workspace: device scratch of at least fos_quantize_workspace_bytes() bytes,
+ *   16-byte aligned, owned by the caller; calls that may overlap need their own.
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_WORKSPACE,
+ * FOS_E_HIP. */
 fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows,
                         int64_t cols, uint8_t* row_data, uint8_t* row_scales,
                         uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
@@ -179,7 +203,9 @@ fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream);
  * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
 fos_status fos_selftest_e2m1_sr(unsigned long long* mismatches, void* stream);
 
-/* Dequantize one NVFP4 record: out[r][c] = RN_fp32(E2M1(q) * RN_fp32(E4M3(s) * t))
+/* Dequantize one NVFP4 record (Ultralytics glossary "FP4", "How FP4 works": a value
+ * is its E2M1 code times its block's E4M3 scale times the tensor's FP32 scale):
+ *   out[r][c] = RN_fp32(E2M1(q) * RN_fp32(E4M3(s) * t))
  * with the nibble's sign (-0 for code 8); FOS_OUT_BF16 rounds that fp32 value to
  * bf16 (nearest-even).  Works for row-wise, column-wise (giving X^T) and 2D records.
  *   data [rows][cols/2] (8-byte aligned), scales [rows][cols/16], tensor_scale: one

@@ -30,20 +30,31 @@ def e2m1_value(nibble: np.ndarray) -> np.ndarray:
     return np.where((nib & 8) != 0, -mag, mag)
 
 
-def _nearest_even(values: np.ndarray, table: np.ndarray) -> np.ndarray:
+def _nearest(values: np.ndarray, table: np.ndarray, ties: str) -> np.ndarray:
     """Index of the nearest entry of the increasing ``table`` to each value (fp64
-    exact distances); an exact tie between two entries goes to the even index;
-    values beyond the last entry map to the last entry (saturation)."""
+    exact distances).  An exact tie between two entries goes to the even index
+    (``ties="even"``) or to the lower entry (``ties="lower"``); values beyond the last
+    entry map to the last entry (saturation)."""
     v = np.asarray(values, dtype=np.float64)
     hi = np.searchsorted(table, v, side="left")          # table[hi-1] < v <= table[hi]
     hi = np.clip(hi, 0, len(table) - 1)
     lo = np.clip(hi - 1, 0, len(table) - 1)
     d_lo = np.abs(v - table[lo])
     d_hi = np.abs(table[hi] - v)
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    if ties == "even":
+        tie_hi = hi % 2 == 0
+    elif ties == "lower":
+        tie_hi = np.zeros(v.shape, dtype=bool)
+    else:
+        raise ValueError(ties)
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & tie_hi)
     idx = np.where(pick_hi, hi, lo)
     idx = np.where(v >= table[-1], len(table) - 1, idx)
     return idx.astype(np.int64)
+
+
+def _nearest_even(values: np.ndarray, table: np.ndarray) -> np.ndarray:
+    return _nearest(values, table, "even")
 
 
 def e2m1_rne_code(magnitude: np.ndarray) -> np.ndarray:
@@ -52,6 +63,17 @@ def e2m1_rne_code(magnitude: np.ndarray) -> np.ndarray:
     m = np.asarray(magnitude, dtype=np.float64)
     assert np.all(m >= 0) and np.all(np.isfinite(m))
     return _nearest_even(m, E2M1_GRID).astype(np.uint8)
+
+
+def e2m1_nearest_lower_code(magnitude: np.ndarray) -> np.ndarray:
+    """Magnitude code (0..7) of the nearest E2M1 value to |v|, an exact tie going to
+    the smaller magnitude (0.25 -> 0, 0.75 -> 0.5, 1.75 -> 1.5, 3.5 -> 3, ...),
+    saturating at 6.  This is the rule of the worked example on the Ultralytics
+    glossary page "FP4" (§How FP4 works), which picks the first grid point at the
+    smallest distance.  Input must be finite and >= 0."""
+    m = np.asarray(magnitude, dtype=np.float64)
+    assert np.all(m >= 0) and np.all(np.isfinite(m))
+    return _nearest(m, E2M1_GRID, "lower").astype(np.uint8)
 
 
 # ---- E4M3 (OCP FN) ---------------------------------------------------------------

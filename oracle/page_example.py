@@ -1,49 +1,51 @@
 """The worked example of block-size error on the Ultralytics glossary page "FP4",
-§How FP4 works.
+§How FP4 works -- TEST INFRASTRUCTURE (part of the oracle).
 
-The page rounds a 4096-value tensor (N(0,1), torch seed 0, every 512th value times
-20) onto the E2M1 grid three times: with one scale for the whole tensor, with one
-scale per 32 values (the MXFP4 block size) and with one per 16 values (the NVFP4
-block size).  Each scale is the block's largest magnitude divided by 6, values take
-the nearest grid point (the first one on equal distance, i.e. the lower magnitude),
-and the printed figure is the mean absolute error of the dequantized tensor.
+The section rounds a 4096-value tensor onto the E2M1 grid three times, with one scale
+for the whole tensor, with one scale per 32 values (MXFP4's block size) and with one
+per 16 values (NVFP4's), and prints the mean absolute error of each.  In its words,
+a block's scale is the one that maps the block's largest magnitude to 6, the largest
+E2M1 value, and every value becomes the nearest grid point of value / scale.  Its
+example picks the first of two equally distant grid points, i.e. the smaller
+magnitude; ``formats.e2m1_nearest_lower_code`` states that rule.
 
-This module restates that recipe in float32 NumPy, plus the same measurement for the
-NVFP4 codec of ``nvfp4.py`` (E4M3 block scales under an FP32 tensor scale, 6-only
-and 4/6 rules) so that the codec can be set beside the page's numbers.
+``block_scale_mae`` restates the measurement with the oracle's own pieces, in fp32
+like the page; ``nvfp4_errors`` takes the same measurement for the NVFP4 codec of
+``nvfp4.py`` (E4M3 block scales under an FP32 tensor scale, 6-only and 4/6 rules) so
+that the codec can be set beside the page's numbers.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import E2M1_GRID, f32_to_bf16_bits, bf16_bits_to_f32
+from .formats import E2M1_GRID, bf16_bits_to_f32, e2m1_nearest_lower_code, f32_to_bf16_bits
 from .nvfp4 import Config, dequantize, quantize
 
 F32 = np.float32
 
 
-def page_recipe_mae(x: np.ndarray, block: int) -> float:
-    """Mean absolute error of the page's rule: scale = amax/6 per block (fp32),
-    nearest grid point with ties to the lower magnitude, value = grid * sign * scale."""
-    x = np.asarray(x, dtype=F32)
-    blocks = x.reshape(-1, block)
-    scale = (np.max(np.abs(blocks), axis=1, keepdims=True) / F32(6.0)).astype(F32)
-    ratio = (np.abs(blocks) / scale).astype(F32)
-    dist = np.abs(ratio[..., None] - E2M1_GRID.astype(F32)).astype(F32)
-    idx = np.argmin(dist, axis=-1)                        # first minimum
-    deq = (E2M1_GRID.astype(F32)[idx] * np.sign(blocks)).astype(F32)
-    deq = (deq * scale).astype(F32)
-    return float(np.mean(np.abs(deq.reshape(-1).astype(np.float64) - x.astype(np.float64))))
+def block_scale_mae(x: np.ndarray, block: int) -> float:
+    """Mean absolute error of one max -> 6 scale per ``block`` consecutive values.
 
-
-def page_recipe_mse(x: np.ndarray, block: int) -> float:
-    x = np.asarray(x, dtype=F32)
-    blocks = x.reshape(-1, block)
-    scale = (np.max(np.abs(blocks), axis=1, keepdims=True) / F32(6.0)).astype(F32)
-    ratio = (np.abs(blocks) / scale).astype(F32)
-    idx = np.argmin(np.abs(ratio[..., None] - E2M1_GRID.astype(F32)), axis=-1)
-    deq = (E2M1_GRID.astype(F32)[idx] * np.sign(blocks) * scale).astype(F32)
-    return float(np.mean((deq.reshape(-1).astype(np.float64) - x.astype(np.float64)) ** 2))
+    For each block: s = RN32(max|x| / 6); each value's magnitude is divided by s in
+    fp32 and mapped to its nearest grid point (ties to the smaller magnitude); the
+    reconstruction is the grid value times s with the value's sign, in fp32.  The
+    error is averaged over all values in fp64.  A block of zeros reconstructs as
+    zeros (no scale is needed for it)."""
+    x = np.asarray(x, dtype=F32).reshape(-1)
+    assert x.size % block == 0
+    err = np.empty(x.size, dtype=np.float64)
+    for b0 in range(0, x.size, block):
+        v = x[b0:b0 + block]
+        s = F32(np.max(np.abs(v)) / F32(6.0))
+        if s == 0:
+            rec = np.zeros(block, dtype=F32)
+        else:
+            code = e2m1_nearest_lower_code((np.abs(v) / s).astype(F32))
+            rec = (E2M1_GRID[code].astype(F32) * s).astype(F32)
+            rec = np.where(np.signbit(v), -rec, rec)
+        err[b0:b0 + block] = np.abs(rec.astype(np.float64) - v.astype(np.float64))
+    return float(np.mean(err))
 
 
 def nvfp4_errors(x: np.ndarray, rule: str):

@@ -31,6 +31,30 @@ def test_library_exports_every_declared_symbol():
         assert getattr(fos.lib(), n).argtypes is not None, n
 
 
+# The calls the boundary must export: quantize, dequantize, the simulated quantized
+# linear forward, the workspace query of quantize, and the status names.
+BOUNDARY_CALLS = ("fos_quantize", "fos_dequantize", "fos_qlinear_fwd",
+                  "fos_quantize_workspace_bytes", "fos_status_string")
+
+
+def test_boundary_calls_exported_and_documented():
+    names = declared_symbols()
+    out = subprocess.run(["nm", "-D", "--defined-only", fos.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fos_\w+)", out))
+    text = open(os.path.join(ROOT, "include", "fos.h")).read()
+    for n in BOUNDARY_CALLS:
+        assert n in names and n in exported, n
+        # the comment right above the declaration cites a page section
+        decl = re.search(r"/\*((?:(?!\*/).)*)\*/\s*(?:const char\*|size_t|fos_status)\s+" + n + r"\s*\(",
+                         text, flags=re.S)
+        assert decl is not None, n
+        comment = re.sub(r"\s*\n\s*\*?\s*", " ", decl.group(1))    # one line of text
+        if n != "fos_status_string":
+            assert '"How FP4 works"' in comment or '"Four Over Six"' in comment, n
+    assert fos.lib().fos_quantize_workspace_bytes() == fos.lib().fos_workspace_bytes()
+
+
 def test_abi_version_and_strings():
     assert fos.ABI_VERSION == 2
     for s in range(7):

@@ -37,7 +37,7 @@ def test_page_worked_example_printed_errors():
     golden = json.load(open(os.path.join(HERE, "golden", "page_fp4_worked_example.json")))
     x = W.page_example().numpy()
     for block, want in golden["mae_printed"].items():
-        got = PE.page_recipe_mae(x, int(block))
+        got = PE.block_scale_mae(x, int(block))
         assert round(got, golden["decimals"]) == want, (block, got, want)
 
 
@@ -45,13 +45,28 @@ def test_nvfp4_codec_on_worked_example_keeps_ordering_and_magnitude():
     x = W.page_example().numpy()
     mae6, mse6 = PE.nvfp4_errors(x, "6")
     mae46, mse46 = PE.nvfp4_errors(x, "4/6")
-    one_scale = PE.page_recipe_mae(x, 4096)
-    b32 = PE.page_recipe_mae(x, 32)
+    one_scale = PE.block_scale_mae(x, 4096)
+    b32 = PE.block_scale_mae(x, 32)
     # 16-value blocks with E4M3 scales stay below the single-scale and 32-block errors
     for mae in (mae6, mae46):
         assert mae < b32 < one_scale
         assert abs(mae - 0.0747) / 0.0747 < 0.25      # page's 16-block magnitude
     assert mse46 <= mse6                             # 4/6 never increases squared error
+
+
+def test_page_tie_rule_is_nearest_with_ties_to_the_smaller_magnitude():
+    """The worked example's rounding: nearest grid point, first (smaller) one on an
+    exact tie; checked by brute force over every midpoint and around it."""
+    grid = F.E2M1_GRID
+    mids = (grid[:-1] + grid[1:]) / 2
+    assert np.array_equal(F.e2m1_nearest_lower_code(mids), np.arange(7))
+    for m, i in zip(mids, range(7)):
+        above = np.nextafter(m, np.inf)
+        assert F.e2m1_nearest_lower_code(np.array([above]))[0] == i + 1
+    rng = np.random.default_rng(12)
+    v = np.concatenate([rng.uniform(0, 8, 20000), grid, [100.0]])
+    want = np.array([int(np.argmin(np.abs(grid - a))) for a in v])   # first minimum
+    assert np.array_equal(F.e2m1_nearest_lower_code(v), want)
 
 
 # ------------------------------------------------------------------ closed forms
@@ -267,6 +282,62 @@ def test_hadamard_option_rotates_before_quantizing():
     assert np.array_equal(q["row_scales"], q2["row_scales"])
 
 
+# ------------------------------------------------------------------ sampled rows
+
+SAMPLED_CFGS = [N.Config(), N.Config(rule="6"), N.Config(rounding="sr", sr_seed=1234),
+                N.Config(hadamard=True, hadamard_seed=5),
+                N.Config(hadamard=True, hadamard_seed=0, rounding="sr", sr_seed=2 ** 40 + 7)]
+
+
+@pytest.mark.parametrize("cfg", SAMPLED_CFGS, ids=["rne", "six", "sr", "rht", "rht_sr"])
+def test_sampled_rows_equal_whole_tensor_rows(cfg):
+    """quantize_rows_sampled (the expectation of the full-size GPU checks) gives, on
+    any row subset -- unsorted, with gaps, first and last row included -- the rows of
+    the whole-tensor quantize under the same tensor scale."""
+    x = _rand(1024, 1024, 21, scale=0.3)                 # 2 MiB of bf16
+    _, t = N.prepare(x, cfg)
+    whole = N.quantize(x, cfg, t=t)
+    assert whole["t"] == t
+    rng = np.random.default_rng(22)
+    rows = np.concatenate([[1023, 0], rng.choice(np.arange(1, 1023), 61, replace=False)])
+    assert not np.all(np.diff(rows) > 0)                 # not sorted
+    got = N.quantize_rows_sampled(x, cfg, t, rows)
+    assert np.array_equal(got["row_data"], whole["row_data"][rows])
+    assert np.array_equal(got["row_scales"], whole["row_scales"][rows])
+
+
+def test_sampled_rows_block_ids_past_two_to_the_32(monkeypatch):
+    """Stochastic-rounding draws of row r, block j use the row-major flat block id
+    r * (C / 16) + j (uint64).  With C = 256 (16 blocks per row) the ids of rows near
+    2^28 pass 2^32; a tensor of 2^28 + 64 rows is emulated by one repeated row (zero
+    row stride), and the ids handed to the draw generator are compared with Python's
+    exact integers."""
+    C = 256
+    base = _rand(1, C, 23)
+    R = (1 << 28) + 64
+    x = np.lib.stride_tricks.as_strided(base, shape=(R, C), strides=(0, base.strides[1]))
+    rows = np.array([(1 << 28) + 63, (1 << 28) - 1, 5, (1 << 28)], dtype=np.int64)
+    seen = []
+    real = N.sr_bytes
+
+    def spy(ids, seed, stream):
+        seen.append(np.array(ids, dtype=np.uint64))
+        return real(ids, seed, stream)
+    monkeypatch.setattr(N, "sr_bytes", spy)
+    cfg = N.Config(rounding="sr", sr_seed=99)
+    got = N.quantize_rows_sampled(x, cfg, F32(0.01), rows)
+    want = np.array([int(r) * (C // 16) + j for r in rows for j in range(C // 16)], dtype=np.uint64)
+    assert len(seen) == 1 and np.array_equal(seen[0], want)
+    assert int(want.max()) >= 2 ** 32 and int(want.min()) < 2 ** 32
+    # rows with the same values but different ids get different draws and codes
+    assert not np.array_equal(got["row_data"][0], got["row_data"][1])
+    # and a row's codes equal those of the same values quantized as blocks with those ids
+    blocks = F.bf16_bits_to_f32(base).reshape(-1, 16)
+    q, S, _, _, _ = N.quantize_blocks(blocks, F32(0.01), "4/6", real(want[:16], 99, 0))
+    assert np.array_equal(got["row_data"][0], N.pack_nibbles(q).reshape(-1))
+    assert np.array_equal(got["row_scales"][0], S)
+
+
 # ------------------------------------------------------------------ stochastic rounding
 
 def test_sr_keeps_grid_values_and_is_unbiased():
@@ -308,6 +379,35 @@ def test_sr_position_is_truncated_to_22_fraction_bits():
     assert up(2.0 ** -10 + 2.0 ** -23, 0)
     assert not up(3.0 - 2.0 ** -9, 255)
     assert up(float(np.nextafter(np.float32(3.0 - 2.0 ** -9), np.float32(4.0))), 255)
+
+
+def test_sr_draw_resolution_edges():
+    """With one 8-bit draw per element the chance of rounding up is the number of draw
+    bytes k with (k + 0.5) / 256 < p22, over 256.  Positions below 1/512 (and exactly
+    1/512: the comparison is strict) never round up; positions above 511/512 always
+    do; elsewhere the chance is within 2^-9 of p (plus the 2^-22 truncation), and the
+    bias 2^-9 is reached at p = 1/512.  Checked exhaustively over the 256 draws on the
+    step [2, 3), where p = |v| - 2 is exact in fp32."""
+    k = np.arange(256)
+    grid = F.E2M1_GRID
+
+    def chance(p):
+        v = np.float32(2.0 + p)
+        assert np.float64(v) - 2.0 == p
+        codes = N.e2m1_sr_code(np.full(256, np.float64(v)), k)
+        return np.mean(grid[codes] > 2.0)
+    for p in (2.0 ** -20, 2.0 ** -10, 1 / 512 - 2.0 ** -20, 1 / 512):
+        assert chance(p) == 0.0, p
+    assert chance(1 / 512 + 2.0 ** -20) == 1 / 256
+    for p in (511 / 512 + 2.0 ** -20, 1 - 2.0 ** -21):
+        assert chance(p) == 1.0, p
+    assert chance(511 / 512) == 255 / 256
+    rng = np.random.default_rng(13)
+    ps = np.concatenate([rng.uniform(0, 1, 400), np.arange(1, 512) / 512])
+    ps = np.floor(ps * 2.0 ** 21) / 2.0 ** 21            # exact in fp32 on [2, 3)
+    bias = np.array([abs(chance(p) - p) for p in ps])
+    assert bias.max() <= 2.0 ** -9
+    assert abs(chance(1 / 512) - 1 / 512) == 2.0 ** -9
 
 
 def test_sr_tensor_mean_close_to_input():
