@@ -120,23 +120,24 @@ int grid_for(int64_t work_items, int per_thread, int cap) {
 
 }  // namespace
 
+int tensor_scale_partials(int64_t rows, int64_t cols, bool hadamard, bool hadamard_cols) {
+  const int64_t n = rows * cols;
+  if (!hadamard) return grid_for(n / 8, kUnroll, kFlatMaxGrid);
+  if (!hadamard_cols) return grid_for(n / 16, 2, kMaxPartials);
+  return grid_for((rows / 16) * (cols / 8), 1, kMaxPartials);
+}
+
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, bool hadamard,
                                bool hadamard_cols, uint32_t rht_mask, float* partials,
                                bool finalize, float* tscale, int* npartials,
                                hipStream_t stream) {
   const int64_t n = rows * cols;
-  int g;
+  const int g = tensor_scale_partials(rows, cols, hadamard, hadamard_cols);
   if (!hadamard) {
-    const int64_t n16 = n / 8;
-    g = grid_for(n16, kUnroll, kFlatMaxGrid);
-    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n16, partials);
+    amax_flat_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n / 8, partials);
   } else if (!hadamard_cols) {
-    const int64_t nblk = n / 16;
-    g = grid_for(nblk, 2, kMaxPartials);
-    amax_rht_rows_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, nblk, rht_mask, partials);
+    amax_rht_rows_kernel<<<g, kThreads, 0, stream>>>((const uint4*)x, n / 16, rht_mask, partials);
   } else {
-    const int64_t npatch = (rows / 16) * (cols / 8);
-    g = grid_for(npatch, 1, kMaxPartials);
     amax_rht_cols_kernel<<<g, kThreads, 0, stream>>>(x, rows, cols, rht_mask, partials);
   }
   if (finalize) scale_finalize_kernel<<<1, kThreads, 0, stream>>>(partials, g, tscale);

@@ -4,8 +4,19 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
+
+// Scratch of fos_quantize_noalloc: the partial maxima of the tensor-scale pass, in a
+// device array that the library owns, so that the call allocates nothing and needs
+// no workspace argument.  Each GPU holds its own copy (at its own address) until the
+// process ends.  On the host `scratch` only names the symbol: its device address
+// comes from hipGetSymbolAddress, once per device (scratch_ptr below).
+constexpr int kScratchFloats = fos::kMaxPartials;
+static __device__ __align__(256) float scratch[kScratchFloats];
 
 namespace {
 
@@ -79,6 +90,39 @@ fos_status check_scale_and_workspace(const float* tscale, const void* ws, size_t
   if (!tscale) return FOS_E_NULL;
   if (!aligned(tscale, 4)) return FOS_E_ALIGN;
   if (!ws || ws_bytes < kWorkspaceBytes || !aligned(ws, 16)) return FOS_E_WORKSPACE;
+  return FOS_OK;
+}
+
+// Device address of `scratch` on the device that runs `stream` (the current device
+// for the null stream).  Looked up with that device current the first time it is
+// needed on the device, then kept.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+fos_status scratch_ptr(hipStream_t stream, float** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FOS_E_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return FOS_E_HIP;
+    dev = d;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return FOS_E_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      if (dev != cur && hipSetDevice(dev) != hipSuccess) return FOS_E_HIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (dev != cur && hipSetDevice(cur) != hipSuccess) return FOS_E_HIP;
+      if (e != hipSuccess || !p) return FOS_E_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = static_cast<float*>(p);
   return FOS_OK;
 }
 
@@ -178,6 +222,45 @@ fos_status check_dequantize(const uint8_t* data, const uint8_t* scales, const fl
   return FOS_OK;
 }
 
+// Validation shared by fos_quantize and fos_quantize_noalloc (all but the workspace).
+fos_status check_quantize(const fos_quant_config* cfg, const void* x, int64_t rows, int64_t cols,
+                          uint8_t* row_data, uint8_t* row_scales, uint8_t* col_data,
+                          uint8_t* col_scales, const float* tensor_scale) {
+  fos_status st = check_config(cfg);
+  if (st != FOS_OK) return st;
+  if ((st = check_input(cfg, x, rows, cols)) != FOS_OK) return st;
+  if (!tensor_scale) return FOS_E_NULL;
+  if (!aligned(tensor_scale, 4)) return FOS_E_ALIGN;
+  if ((st = check_outputs(cfg, rows, cols, row_data, row_scales, col_data, col_scales)) != FOS_OK)
+    return st;
+  const fos::QuantArgs a =
+      make_args(cfg, x, rows, cols, nullptr, row_data, row_scales, col_data, col_scales);
+  if (fos::quantize_grid(a) > fos::kMaxGrid) return FOS_E_SHAPE;
+  return FOS_OK;
+}
+
+// The tensor-scale pass into `scratch` (partial maxima), then the quantize kernel, which
+// reduces them; arguments already validated.
+fos_status quantize_validated(const fos_quant_config* cfg, const void* x, int64_t rows,
+                              int64_t cols, uint8_t* row_data, uint8_t* row_scales,
+                              uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
+                              float* scratch_mem, hipStream_t s) {
+  fos::QuantArgs a =
+      make_args(cfg, x, rows, cols, nullptr, row_data, row_scales, col_data, col_scales);
+  // an empty tensor launches no quantize kernel: the scale pass writes t (= 0) itself
+  const bool empty = rows * cols == 0;
+  int npartials = 0;
+  fos_status st;
+  if ((st = launch_scale(cfg, x, rows, cols, tensor_scale, scratch_mem, empty, &npartials, s)) !=
+      FOS_OK)
+    return st;
+  if (empty) return FOS_OK;
+  a.partials = scratch_mem;
+  a.npartials = npartials;
+  a.tscale_out = tensor_scale;
+  return fos::launch_quantize(a, s) == hipSuccess ? FOS_OK : FOS_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,23 +323,31 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
   if ((st = check_input(cfg, x, rows, cols)) != FOS_OK) return st;
   if ((st = check_scale_and_workspace(tensor_scale, workspace, workspace_bytes)) != FOS_OK)
     return st;
-  if ((st = check_outputs(cfg, rows, cols, row_data, row_scales, col_data, col_scales)) != FOS_OK)
+  if ((st = check_quantize(cfg, x, rows, cols, row_data, row_scales, col_data, col_scales,
+                           tensor_scale)) != FOS_OK)
     return st;
-  fos::QuantArgs a =
-      make_args(cfg, x, rows, cols, nullptr, row_data, row_scales, col_data, col_scales);
-  if (fos::quantize_grid(a) > fos::kMaxGrid) return FOS_E_SHAPE;
+  return quantize_validated(cfg, x, rows, cols, row_data, row_scales, col_data, col_scales,
+                            tensor_scale, static_cast<float*>(workspace),
+                            static_cast<hipStream_t>(stream));
+}
+
+fos_status fos_quantize_noalloc(const fos_quant_config* cfg, const void* x, int64_t rows,
+                                int64_t cols, uint8_t* row_data, uint8_t* row_scales,
+                                uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
+                                void* stream) {
+  fos_status st = check_quantize(cfg, x, rows, cols, row_data, row_scales, col_data, col_scales,
+                                 tensor_scale);
+  if (st != FOS_OK) return st;
+  // the scale pass writes at most kMaxPartials partial maxima, whatever the shape; a
+  // pass that needed more than `scratch` holds is refused before anything runs
+  if (fos::tensor_scale_partials(rows, cols, cfg->hadamard != 0,
+                                 cfg->hadamard != 0 && wants_cols(cfg)) > kScratchFloats)
+    return FOS_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // an empty tensor launches no quantize kernel: the scale pass writes t (= 0) itself
-  const bool empty = rows * cols == 0;
-  int npartials = 0;
-  if ((st = launch_scale(cfg, x, rows, cols, tensor_scale, workspace, empty, &npartials, s)) !=
-      FOS_OK)
-    return st;
-  if (empty) return FOS_OK;
-  a.partials = static_cast<const float*>(workspace);
-  a.npartials = npartials;
-  a.tscale_out = tensor_scale;
-  return fos::launch_quantize(a, s) == hipSuccess ? FOS_OK : FOS_E_HIP;
+  float* mem = nullptr;
+  if ((st = scratch_ptr(s, &mem)) != FOS_OK) return st;
+  return quantize_validated(cfg, x, rows, cols, row_data, row_scales, col_data, col_scales,
+                            tensor_scale, mem, s);
 }
 
 fos_status fos_selftest_e4m3(unsigned long long* mismatches, void* stream) {

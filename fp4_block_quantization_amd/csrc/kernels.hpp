@@ -26,6 +26,10 @@ struct QuantArgs {
   bool hadamard;
 };
 
+// Number of partial maxima the tensor-scale pass writes for this shape (a multiple
+// of 4, at least 4 and at most kMaxPartials).
+int tensor_scale_partials(int64_t rows, int64_t cols, bool hadamard, bool hadamard_cols);
+
 // Tensor-scale pass: one partial max|x| per workgroup into `partials` (16-byte
 // aligned; the count, a multiple of 4 and at most kMaxPartials, goes to *npartials).
 // With `finalize`, a one-workgroup kernel then writes t = max / 2688 to *tscale;

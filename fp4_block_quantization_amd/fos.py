@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "fos_tensor_scale": ([cfgp, P, I64, I64, P, P, SZ, P], ctypes.c_int),
         "fos_quantize_scaled": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
         "fos_quantize": ([cfgp, P, I64, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "fos_quantize_noalloc": ([cfgp, P, I64, I64, P, P, P, P, P, P], ctypes.c_int),
         "fos_selftest_e4m3": ([P, P], ctypes.c_int),
         "fos_selftest_e2m1": ([P, P], ctypes.c_int),
         "fos_selftest_e2m1_sr": ([P, P], ctypes.c_int),
@@ -158,6 +159,16 @@ def fos_quantize(cfg: FosQuantConfig, x: torch.Tensor, row_data, row_scales, col
                              _ptr(row_data), _ptr(row_scales), _ptr(col_data), _ptr(col_scales),
                              _ptr(tensor_scale), _ptr(ws), ws.numel(), _stream(x.device)),
            "fos_quantize")
+
+
+def fos_quantize_noalloc(cfg: FosQuantConfig, x: torch.Tensor, row_data, row_scales, col_data,
+                         col_scales, tensor_scale: torch.Tensor) -> None:
+    """fos_quantize without a workspace: the library's own per-GPU scratch array holds
+    the tensor-scale pass's partial maxima (calls on one GPU must not overlap)."""
+    _check(_lib.fos_quantize_noalloc(ctypes.byref(cfg), _ptr(x), x.shape[0], x.shape[1],
+                                     _ptr(row_data), _ptr(row_scales), _ptr(col_data),
+                                     _ptr(col_scales), _ptr(tensor_scale), _stream(x.device)),
+           "fos_quantize_noalloc")
 
 
 def selftest_e4m3(device="cuda:0") -> int:

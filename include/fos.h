@@ -167,6 +167,25 @@ fos_status fos_quantize(const fos_quant_config* cfg, const void* x, int64_t rows
                         uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* fos_quantize for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same results.  The
+ * tensor-scale pass keeps its partial maxima in a 4096-byte device array that the
+ * library holds on each GPU it runs on until the process ends (1024 fp32 partial
+ * maxima; the pass never needs more, for any shape the other checks accept, and a
+ * pass that would is refused with FOS_E_WORKSPACE).  The call allocates nothing
+ * and frees nothing; its first call on a device looks the array's address up.
+ * Every call on one GPU shares that array: calls that may overlap on one GPU
+ * (different streams, or other threads) race and must be ordered by the caller.
+ * Nothing in the array needs clearing between calls (every partial is written
+ * before it is read).
+ * Errors: FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_WORKSPACE,
+ * FOS_E_HIP. */
+fos_status fos_quantize_noalloc(const fos_quant_config* cfg, const void* x, int64_t rows,
+                                int64_t cols, uint8_t* row_data, uint8_t* row_scales,
+                                uint8_t* col_data, uint8_t* col_scales, float* tensor_scale,
+                                void* stream);
+
 /* Self-test of the hardware E4M3 conversion that the quantize kernels use for the
  * block scales (gfx950's packed fp32 -> OCP E4M3 conversion, nearest-even): adds to
  * *mismatches (device uint64, 8-byte aligned; the caller zeroes it) the number of
