@@ -285,10 +285,15 @@ def _check_record(q, *others):
 
 
 def tensor_scale(x: torch.Tensor, hadamard_seed: Optional[int] = None,
-                 outputs: Sequence[str] = ("row",)) -> torch.Tensor:
+                 outputs: Sequence[str] = ("row",), out: Optional[torch.Tensor] = None
+                 ) -> torch.Tensor:
+    """The per-tensor FP32 scale t of x (device fp32 [1]), on the current stream;
+    ``out``: optional destination."""
     _check_input(x)
     cfg = make_config(outputs=outputs, hadamard_seed=hadamard_seed)
-    t = torch.empty(1, dtype=torch.float32, device=x.device)
+    t = out if out is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    if t.dtype != torch.float32 or t.numel() != 1 or t.device != x.device:
+        raise ValueError("out must be a one-element fp32 tensor on x's device")
     fos_tensor_scale(cfg, x, t)
     return t
 

@@ -122,7 +122,48 @@ def test_qlinear_act_full_size_c5_sampled(fos):
     ow = N.quantize_rows_sampled(wb, cfg, tw, cols)
     assert_same_bytes(xr.data.cpu().numpy()[rows], ox["row_data"], "x record data")
     assert_same_bytes(xr.scales.cpu().numpy()[rows], ox["row_scales"], "x record scales")
-    y64 = qlinear_ref64(ox["row_data"], ox["row_scales"], tx, ow["row_data"], ow["row_scales"], tw)
-    yg = F.bf16_bits_to_f32(bits_of(y.cpu())[np.ix_(rows, cols)]).astype(np.float64)
-    ref16 = F.bf16_bits_to_f32(F.f32_to_bf16_bits(y64.astype(np.float32))).astype(np.float64)
-    assert np.linalg.norm(yg - ref16) / np.linalg.norm(y64) <= 1e-3
+    _qlinear_check(bits_of(y.cpu())[np.ix_(rows, cols)], ox["row_data"], ox["row_scales"], tx,
+                   ow["row_data"], ow["row_scales"], tw)
+
+
+def test_scale_pass_overlapped_with_the_previous_layer(fos):
+    """Inference pipelining of the activation's tensor scale: while the previous layer's
+    GEMM runs on the main stream, fos_tensor_scale(X) runs on a second stream; after an
+    event wait the main stream runs fos_qlinear_fwd_act with the scale given, so X is
+    read once.  The overlapped run must give X's record bit-exact with the oracle, Y
+    within tolerance, and the previous layer's output unchanged."""
+    m, n, k = 2048, 3072, 4096
+    xb = bits_of(W.random_bf16(m, k, 111, "student_t", scale=0.5))
+    pb = bits_of(W.random_bf16(m, k, 113, "student_t"))             # previous layer's input
+    wb = bits_of(W.random_bf16(n, k, 115, "normal", scale=0.02))
+    ow, wq = _weight_record(fos, wb, N.Config())
+    pq = fos.quantize(to_gpu_bf16(pb))
+    x = to_gpu_bf16(xb)
+    y_prev_alone = fos.qlinear_fwd(pq, wq)
+    torch.cuda.synchronize()
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    t_x = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    side.wait_stream(main)                  # x, t_x and the records are ready
+    y_prev = torch.empty_like(y_prev_alone)
+    fos.qlinear_fwd(pq, wq, out=y_prev)                      # previous layer, main stream
+    with torch.cuda.stream(side):
+        fos.tensor_scale(x, out=t_x)                         # X's scale pass, side stream
+        done = torch.cuda.Event()
+        done.record(side)
+    main.wait_event(done)
+    y, xr = fos.qlinear_fwd_act(x, wq, x_tensor_scale=t_x, return_record=True)
+    torch.cuda.synchronize()
+
+    assert torch.equal(y_prev, y_prev_alone)
+    ox = N.quantize(xb, N.Config())
+    assert np.float32(t_x.cpu()[0]).view(np.uint32) == np.float32(ox["t"]).view(np.uint32)
+    assert_same_bytes(xr.data.cpu().numpy(), ox["row_data"], "x record data")
+    assert_same_bytes(xr.scales.cpu().numpy(), ox["row_scales"], "x record scales")
+    rows = _sample_rows(m, 48, 13)
+    cols = _sample_rows(n, 48, 14)
+    sub = lambda o, r: {"row_data": o["row_data"][r], "row_scales": o["row_scales"][r]}
+    sx, sw = sub(ox, rows), sub(ow, cols)
+    _qlinear_check(bits_of(y.cpu())[np.ix_(rows, cols)], sx["row_data"], sx["row_scales"], ox["t"],
+                   sw["row_data"], sw["row_scales"], ow["t"])
