@@ -185,7 +185,7 @@ class QuantCase:
         self.bad |= self._ts(*self.args_ts[i])
 
 
-def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.0):
+def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.2):
     R, C = x_cpu.shape
     sets = min(8, max(3, -(-300 * 2 ** 20 // (2 * R * C))))   # > 256 MB of inputs rotate
     case = QuantCase(fos, x_cpu, cfg_kw, sets)
@@ -333,6 +333,58 @@ def bench_qlinear_act(fos, x_cpu, w_cpu, steps, warmup):
     return out
 
 
+def bench_qlinear_overlap(fos, x_cpu, w_cpu, steps, warmup):
+    """The inference pipelining of the activation's tensor scale, on the c5 shapes: a
+    previous layer's GEMM (fos_qlinear_fwd on quantized input) followed by this layer
+    from bf16 X (fos_qlinear_fwd_act with X's scale given, so X is read once).
+    sequential: X's scale pass, the previous GEMM and this layer on one stream.
+    overlapped: the scale pass on a second stream beside the previous GEMM; this layer
+    waits for it on an event.  per_layer = overlapped - the previous GEMM alone."""
+    import torch
+    dev = "cuda:0"
+    x = x_cpu.to(dev)
+    wq = fos.quantize(w_cpu.to(dev))
+    pq = fos.quantize(x)                          # the previous layer's quantized input
+    M, K = x.shape
+    N = wq.shape[0]
+    y_prev = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    t = torch.zeros(1, dtype=torch.float32, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        fos.tensor_scale(x, out=t)               # the side stream's workspace, made once
+    torch.cuda.synchronize()
+
+    def prev_gemm(i):
+        fos.qlinear_fwd(pq, wq, out=y_prev)
+
+    def sequential(i):
+        fos.tensor_scale(x, out=t)
+        fos.qlinear_fwd(pq, wq, out=y_prev)
+        fos.qlinear_fwd_act(x, wq, x_tensor_scale=t, out=y)
+
+    def overlapped(i):
+        side.wait_stream(main)                   # t is free once the last layer read it
+        with torch.cuda.stream(side):
+            fos.tensor_scale(x, out=t)
+            ev = torch.cuda.Event()
+            ev.record(side)
+        fos.qlinear_fwd(pq, wq, out=y_prev)
+        main.wait_event(ev)
+        fos.qlinear_fwd_act(x, wq, x_tensor_scale=t, out=y)
+
+    n = max(6, steps // 4)
+    ms_prev = time_loop(prev_gemm, n, max(10, warmup), 1)
+    ms_seq = time_loop(sequential, n, max(5, warmup), 1)
+    ms_ovl = time_loop(overlapped, n, max(5, warmup), 1)
+    flops = 2 * M * N * K
+    return {"shape": [M, N, K], "ms_previous_gemm": ms_prev, "ms_two_layers_sequential": ms_seq,
+            "ms_two_layers_overlapped": ms_ovl, "ms_layer_overlapped": ms_ovl - ms_prev,
+            "TFLOPs_layer_overlapped": flops / (ms_ovl - ms_prev) / 1e9,
+            "ms_scale_pass_hidden": ms_seq - ms_ovl}
+
+
 def bench_qlinear_bwd(fos, x_cpu, w_cpu, dy_cpu, steps, warmup):
     """Backward products of the c5 layer: dX = deq(dY) deq(W^T)^T (inner 12288) and
     dW = deq(dY^T) deq(X^T)^T (inner 8192), from training-style records: dY row and
@@ -408,17 +460,66 @@ def bench_mx(fos, x_cpu, w_cpu, x2_cpu, steps, warmup):
                         "frac_fp4_peak": flops / ms_g / 1e9 / FP4_MFMA_PEAK_TFLOPS}}
 
 
-def copy_reference(steps):
-    """A plain device-to-device copy (torch's copy kernel) of 256 MiB: a measured
-    ceiling for streaming read+write traffic on this GPU."""
-    import torch
-    n = 256 * 2 ** 20
-    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
+CEILING_LIB = os.path.join(ROOT, "fp4_block_quantization_amd", "libfos_ceiling.so")
 
-    def fn(i):
-        bufs[2 * (i % 2) + 1].copy_(bufs[2 * (i % 2)])
-    ms = time_loop(fn, steps, 3, 2)
-    return {"bytes": 2 * n, "ms": ms, "GBps": 2 * n / ms / 1e6, "frac": 2 * n / ms / 1e6 / HBM_PEAK_GBS}
+
+def _ceiling_lib():
+    import ctypes
+    lib = ctypes.CDLL(CEILING_LIB)
+    P, SZ = ctypes.c_void_p, ctypes.c_size_t
+    lib.fos_ceiling_read.argtypes = [P, SZ, ctypes.c_uint32, P, P]
+    lib.fos_ceiling_copy.argtypes = [P, P, SZ, P]
+    lib.fos_ceiling_pattern.argtypes = [P, SZ, P, P, P]
+    return lib
+
+
+class Ceilings:
+    """Hand-written kernels (libfos_ceiling.so) that move the c2 quantize kernel's
+    bytes without computing: a streaming read of the 100.7 MB input, a copy of it
+    (read + write), and the row-wise quantize kernel's exact traffic (read 32 bytes,
+    write 8 + 1 per 16 values).  Three input sets (> 256 MB) rotate."""
+
+    def __init__(self, nbytes, sets=3):
+        import ctypes
+        import torch
+        self.lib = _ceiling_lib()
+        dev = "cuda:0"
+        self.n = nbytes
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.x = [torch.randint(0, 255, (nbytes,), **u8) for _ in range(sets)]
+        self.y = [torch.empty(nbytes, **u8) for _ in range(sets)]
+        self.y8 = [torch.empty(nbytes // 4, **u8) for _ in range(sets)]
+        self.y1 = [torch.empty(nbytes // 32, **u8) for _ in range(sets)]
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        self.sets = sets
+        self.bad = 0
+
+    def read(self, i):
+        self.bad |= self.lib.fos_ceiling_read(_vp(self.x[i]), self.n, 0x9E3779B9, _vp(self.sink),
+                                              self.stream)
+
+    def copy(self, i):
+        self.bad |= self.lib.fos_ceiling_copy(_vp(self.x[i]), _vp(self.y[i]), self.n, self.stream)
+
+    def pattern(self, i):
+        self.bad |= self.lib.fos_ceiling_pattern(_vp(self.x[i]), self.n, _vp(self.y8[i]),
+                                                 _vp(self.y1[i]), self.stream)
+
+
+def bench_ceilings(nbytes, steps, warmup):
+    c = Ceilings(nbytes)
+    rows = {}
+    for name, fn, moved in (("read", c.read, nbytes), ("copy", c.copy, 2 * nbytes),
+                            ("c2_quantize_pattern", c.pattern, nbytes + nbytes // 4 + nbytes // 32)):
+        settle(fn, c.sets, 0.1)
+        ms = time_loop(fn, steps, warmup, c.sets)
+        rows[name] = {"bytes": moved, "ms": ms, "GBps": moved / ms / 1e6,
+                      "frac": moved / ms / 1e6 / HBM_PEAK_GBS}
+    if c.bad:
+        raise RuntimeError("a ceiling kernel returned an error status")
+    del c
+    return rows
 
 
 def cpu_baseline(x_cpu, rows_sample):
@@ -507,7 +608,8 @@ def main():
                     help="profiling aid: run one piece (c2_step, c2_kernel, c3_kernel, c4a_kernel, "
                          "c4b_kernel, c2_dequant_bf16, c2_dequant_f32, c2_mx_dequant_bf16, "
                          "c4a_dequant_hadamard_bf16, c5_qlinear, c5_qlinear_act, "
-                         "c5_qlinear_act_given, c5_mx_gemm, copy) and exit")
+                         "c5_qlinear_act_given, c5_mx_gemm, copy, ceiling_read, ceiling_copy, "
+                         "ceiling_pattern) and exit")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -590,6 +692,16 @@ def main():
             torch.cuda.synchronize()
             log("copy: 268435456 bytes per dispatch")
             return
+        if args.only in ("ceiling_read", "ceiling_copy", "ceiling_pattern"):
+            c = Ceilings(2 * x2.numel())
+            fn = getattr(c, args.only.split("_", 1)[1])
+            for i in range(args.steps):
+                fn(i % c.sets)
+            torch.cuda.synchronize()
+            if c.bad:
+                raise RuntimeError("a ceiling kernel returned an error status")
+            log(f"ran {args.only} x{args.steps} on {c.n} input bytes")
+            return
         kernels = {"c2_kernel": ("c2", {}), "c2_step": ("c2", {}),
                    "c3_kernel": ("c3", {"outputs": ("row", "col")}),
                    "c4a_kernel": ("c4a", {"hadamard_seed": 0, "rounding": "sr", "sr_seed": 1234}),
@@ -630,8 +742,9 @@ def main():
     log("C4b ...")
     rows["c4b_2d"] = bench_quant(fos, "c4b weight 12288x4096, 2D 16x16", W.make("c4b"),
                                  {"block": "2d"}, args.steps, args.warmup)
-    log("copy reference ...")
-    rows["hbm_copy_reference"] = copy_reference(args.steps)
+    log("HBM ceilings ...")
+    rows["hbm_ceilings_c2_bytes"] = bench_ceilings(2 * x2.numel(), args.steps, args.warmup)
+    log(json.dumps(rows["hbm_ceilings_c2_bytes"]))
     log("C5 qlinear ...")
     rows["c5_qlinear"] = bench_qlinear(fos, W.make("c5_x"), W.make("c5_w"), args.steps, args.warmup)
     log(json.dumps(rows["c5_qlinear"]))
@@ -639,6 +752,10 @@ def main():
     rows["c5_qlinear_act"] = bench_qlinear_act(fos, W.make("c5_x"), W.make("c5_w"), args.steps,
                                                args.warmup)
     log(json.dumps(rows["c5_qlinear_act"]))
+    log("C5 layer with the scale pass overlapped ...")
+    rows["c5_qlinear_act_overlap"] = bench_qlinear_overlap(fos, W.make("c5_x"), W.make("c5_w"),
+                                                           args.steps, args.warmup)
+    log(json.dumps(rows["c5_qlinear_act_overlap"]))
     log("C5 qlinear backward ...")
     rows["c5_qlinear_bwd"] = bench_qlinear_bwd(fos, W.make("c5_x"), W.make("c5_w"),
                                                W.make("c5_dy"), args.steps, args.warmup)

@@ -31,6 +31,33 @@ def test_library_exports_every_declared_symbol():
         assert getattr(fos.lib(), n).argtypes is not None, n
 
 
+def test_ceiling_library_exports_and_validates():
+    """libfos_ceiling.so (measured HBM ceilings for the benchmark) exports what
+    include/fos_ceiling.h declares and rejects bad arguments before any launch."""
+    text = open(os.path.join(ROOT, "include", "fos_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(fos_[a-z_0-9]+)\s*\(", text)))
+    path = os.path.join(os.path.dirname(fos.LIB_PATH), "libfos_ceiling.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (fos_\w+)", out))
+    assert len(names) == 4 and set(names) <= exported
+    L = ctypes.CDLL(path)
+    L.fos_ceiling_granule.restype = ctypes.c_size_t
+    g = L.fos_ceiling_granule()
+    assert g == 8192
+    P, SZ = ctypes.c_void_p, ctypes.c_size_t
+    L.fos_ceiling_read.argtypes = [P, SZ, ctypes.c_uint32, P, P]
+    L.fos_ceiling_copy.argtypes = [P, P, SZ, P]
+    L.fos_ceiling_pattern.argtypes = [P, SZ, P, P, P]
+    assert L.fos_ceiling_read(None, g, 0, FAKE, None) == 1
+    assert L.fos_ceiling_read(FAKE, g + 16, 0, FAKE, None) == 2
+    assert L.fos_ceiling_read(FAKE, 0, 0, FAKE, None) == 2
+    assert L.fos_ceiling_copy(MIS, FAKE, g, None) == 3
+    assert L.fos_ceiling_pattern(FAKE, g, ctypes.c_void_p(0x100004), FAKE, None) == 3
+    assert L.fos_ceiling_pattern(FAKE, g, FAKE, None, None) == 1
+
+
 # The calls the boundary must export: quantize, dequantize, the simulated quantized
 # linear forward, the workspace query of quantize, and the status names.
 BOUNDARY_CALLS = ("fos_quantize", "fos_dequantize", "fos_qlinear_fwd",
