@@ -49,6 +49,12 @@ kept; "RN(.)" is one fp32 rounding):
       iff (k + 0.5)/256 < p22.  Both candidates use the same draws and the choice
       compares the errors of the rounded values.
       2D tiles take the draws of the row-wise layout for every output.
+      Full resolution ("sr_full"): element i of block b takes the whole 32-bit word
+      i % 4 of Philox4x32-10(key = sr_seed, counter = (b_lo32, b_hi32, i // 4,
+      stream)), four calls per block; with u = its top 22 bits (word >> 10), the
+      value rounds up iff p22 * 2^22 + u >= 2^22, so it rounds up with probability
+      p22 exactly (p truncated to 22 fractional bits), with no dead zone near the grid
+      points.  Everything else as above.
 
 The element-wise scale uses a per-block reciprocal and the per-block scale uses a
 per-tensor reciprocal (u_c); the error is the exact dequantization error rounded
@@ -76,7 +82,7 @@ MIN_NORMAL = F32(2.0 ** -126)
 @dataclass
 class Config:
     rule: str = "4/6"            # "4/6" or "6"
-    rounding: str = "rne"        # "rne" or "sr"
+    rounding: str = "rne"        # "rne", "sr" (8-bit draws) or "sr_full" (22-bit draws)
     block: str = "1d"            # "1d" or "2d"
     rows_out: bool = True        # row-wise output
     cols_out: bool = False       # column-wise (transposed) output
@@ -105,6 +111,46 @@ def sr_bytes(block_ids: np.ndarray, seed: int, stream: int) -> np.ndarray:
     for i in range(16):
         out[..., i] = (words[..., i // 4] >> np.uint32(8 * (i % 4))) & np.uint32(0xFF)
     return out
+
+
+def sr_words(block_ids: np.ndarray, seed: int, stream: int) -> np.ndarray:
+    """(n,) flat block indices -> (n, 16) uint32 draw words of the full-resolution
+    mode of O9: element i takes word i % 4 of the call with counter word 2 = i // 4."""
+    b = np.asarray(block_ids, dtype=np.uint64)
+    out = np.empty(b.shape + (16,), dtype=np.uint32)
+    for j in range(4):
+        ctr = np.stack([b & np.uint64(0xFFFFFFFF), b >> np.uint64(32),
+                        np.full_like(b, j), np.full_like(b, stream)], axis=-1)
+        words = philox4x32_10(ctr, split_seed(seed))          # (n, 4) uint32
+        out[..., 4 * j:4 * j + 4] = words
+    return out
+
+
+def _grid_position(magnitude: np.ndarray):
+    """For |v| >= 0: the codes of the grid values lo <= |v| < hi (lo == hi == 6 at and
+    above 6) and p = (|v| - lo) / (hi - lo), exact in fp64 (the steps are powers of
+    two)."""
+    m = np.asarray(magnitude, dtype=np.float64)
+    lo = np.searchsorted(E2M1_GRID, m, side="right") - 1     # grid[lo] <= m
+    lo = np.clip(lo, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    step = E2M1_GRID[hi] - E2M1_GRID[lo]
+    p = np.where(step > 0, (m - E2M1_GRID[lo]) / np.where(step > 0, step, 1.0), 0.0)
+    return lo, hi, p
+
+
+def e2m1_sr_full_code(magnitude: np.ndarray, words: np.ndarray) -> np.ndarray:
+    """Full-resolution stochastic rounding of |v| >= 0 onto the E2M1 grid with 32-bit
+    draw words: with P = floor(p * 2^22) (p's first 22 fractional bits) and u = word >>
+    10, |v| rounds up iff P + u >= 2^22.  Over the 2^22 values of u exactly P round up,
+    so the chance is p to within 2^-22.  6 and above give 6."""
+    lo, hi, p = _grid_position(magnitude)
+    P = np.floor(p * 2.0 ** 22).astype(np.int64)
+    u = (np.asarray(words, dtype=np.uint32) >> np.uint32(10)).astype(np.int64)
+    up = (P + u) >= (1 << 22)
+    code = np.where(up, hi, lo)
+    code = np.where(np.asarray(magnitude, dtype=np.float64) >= 6.0, 7, code)
+    return code.astype(np.uint8)
 
 
 def e2m1_sr_code(magnitude: np.ndarray, k: np.ndarray) -> np.ndarray:
@@ -162,7 +208,9 @@ def _candidate(x: np.ndarray, a: np.ndarray, t: F32, c: float,
     vmag = np.abs(v)
     if draws is None:
         m = e2m1_rne_code(vmag.reshape(-1)).reshape(x.shape)
-    else:
+    elif draws.dtype == np.uint32:                 # full-resolution draw words
+        m = e2m1_sr_full_code(vmag.reshape(-1), draws.reshape(-1)).reshape(x.shape)
+    else:                                          # 8-bit draw bytes
         m = e2m1_sr_code(vmag.reshape(-1), draws.reshape(-1)).reshape(x.shape)
     m = np.where(ok.reshape(shape_b), m, np.uint8(0)).astype(np.uint8)
     emag = E2M1_GRID[m]
@@ -258,13 +306,14 @@ def quantize(x_bf16: np.ndarray, cfg: Config, t: Optional[F32] = None):
     t = t_own if t is None else F32(t)
     R, C = x.shape
     out = {"t": t}
-    sr = cfg.rounding == "sr"
+    sr = cfg.rounding in ("sr", "sr_full")
+    draw = sr_words if cfg.rounding == "sr_full" else sr_bytes
     if cfg.block == "2d":
         tiles = x.reshape(R // 16, 16, C // 16, 16).transpose(0, 2, 1, 3).reshape(-1, 16, 16)
         draws = None
         if sr:
             ids = np.arange(R * (C // 16), dtype=np.uint64)   # row-wise block ids
-            draws = sr_bytes(ids, cfg.sr_seed, 0).reshape(R // 16, 16, C // 16, 16)
+            draws = draw(ids, cfg.sr_seed, 0).reshape(R // 16, 16, C // 16, 16)
             draws = draws.transpose(0, 2, 1, 3).reshape(-1, 16, 16)
         q, S, _, _, _ = quantize_blocks(tiles, t, cfg.rule, draws, two_d=True)
         qf = q.reshape(R // 16, C // 16, 16, 16).transpose(0, 2, 1, 3).reshape(R, C)
@@ -278,13 +327,13 @@ def quantize(x_bf16: np.ndarray, cfg: Config, t: Optional[F32] = None):
         return out
     if cfg.rows_out:
         blocks = x.reshape(-1, 16)
-        draws = sr_bytes(np.arange(blocks.shape[0], dtype=np.uint64), cfg.sr_seed, 0) if sr else None
+        draws = draw(np.arange(blocks.shape[0], dtype=np.uint64), cfg.sr_seed, 0) if sr else None
         q, S, _, _, _ = quantize_blocks(blocks, t, cfg.rule, draws)
         out["row_data"] = pack_nibbles(q).reshape(R, C // 2)
         out["row_scales"] = S.reshape(R, C // 16)
     if cfg.cols_out:
         blocks = np.ascontiguousarray(x.T).reshape(-1, 16)
-        draws = sr_bytes(np.arange(blocks.shape[0], dtype=np.uint64), cfg.sr_seed, 1) if sr else None
+        draws = draw(np.arange(blocks.shape[0], dtype=np.uint64), cfg.sr_seed, 1) if sr else None
         q, S, _, _, _ = quantize_blocks(blocks, t, cfg.rule, draws)
         out["col_data"] = pack_nibbles(q).reshape(C, R // 2)
         out["col_scales"] = S.reshape(C, R // 16)
@@ -302,10 +351,10 @@ def quantize_rows_sampled(x_bf16: np.ndarray, cfg: Config, t: F32, row_ids) -> d
         x = rht_blocks(x.reshape(len(row_ids), C // 16, 16), rht_signs(cfg.hadamard_seed)).reshape(len(row_ids), C)
     blocks = x.reshape(-1, 16)
     draws = None
-    if cfg.rounding == "sr":
+    if cfg.rounding in ("sr", "sr_full"):
         ids = (np.asarray(row_ids, dtype=np.uint64)[:, None] * np.uint64(C // 16)
                + np.arange(C // 16, dtype=np.uint64)[None, :]).reshape(-1)
-        draws = sr_bytes(ids, cfg.sr_seed, 0)
+        draws = (sr_words if cfg.rounding == "sr_full" else sr_bytes)(ids, cfg.sr_seed, 0)
     q, S, _, _, _ = quantize_blocks(blocks, F32(t), cfg.rule, draws)
     return {"row_data": pack_nibbles(q).reshape(len(row_ids), C // 2),
             "row_scales": S.reshape(len(row_ids), C // 16)}

@@ -219,7 +219,9 @@ def _rand(rows, cols, seed, scale=1.0):
 
 
 @pytest.mark.parametrize("cfg", [N.Config(), N.Config(rounding="sr", sr_seed=3),
+                                 N.Config(rounding="sr_full", sr_seed=3, cols_out=True),
                                  N.Config(block="2d", cols_out=True),
+                                 N.Config(block="2d", rounding="sr_full", sr_seed=4),
                                  N.Config(hadamard=True, hadamard_seed=11)])
 def test_negation_flips_sign_bits_only(cfg):
     x = _rand(48, 64, 1)
@@ -286,10 +288,11 @@ def test_hadamard_option_rotates_before_quantizing():
 
 SAMPLED_CFGS = [N.Config(), N.Config(rule="6"), N.Config(rounding="sr", sr_seed=1234),
                 N.Config(hadamard=True, hadamard_seed=5),
-                N.Config(hadamard=True, hadamard_seed=0, rounding="sr", sr_seed=2 ** 40 + 7)]
+                N.Config(hadamard=True, hadamard_seed=0, rounding="sr", sr_seed=2 ** 40 + 7),
+                N.Config(rounding="sr_full", sr_seed=77)]
 
 
-@pytest.mark.parametrize("cfg", SAMPLED_CFGS, ids=["rne", "six", "sr", "rht", "rht_sr"])
+@pytest.mark.parametrize("cfg", SAMPLED_CFGS, ids=["rne", "six", "sr", "rht", "rht_sr", "sr_full"])
 def test_sampled_rows_equal_whole_tensor_rows(cfg):
     """quantize_rows_sampled (the expectation of the full-size GPU checks) gives, on
     any row subset -- unsorted, with gaps, first and last row included -- the rows of
@@ -408,6 +411,74 @@ def test_sr_draw_resolution_edges():
     bias = np.array([abs(chance(p) - p) for p in ps])
     assert bias.max() <= 2.0 ** -9
     assert abs(chance(1 / 512) - 1 / 512) == 2.0 ** -9
+
+
+def _sr_full_chance(v):
+    """Fraction of the 2^22 draw values u (low 10 bits of the word set to a fixed
+    pattern, which the rule ignores) for which |v| rounds up under the full-resolution
+    rule, and the up / down values."""
+    u = np.arange(1 << 22, dtype=np.uint32)
+    words = (u << np.uint32(10)) | np.uint32(0x2A5)
+    codes = N.e2m1_sr_full_code(np.full(u.shape, v, dtype=np.float64), words)
+    vals = F.E2M1_GRID[codes]
+    return np.count_nonzero(vals > v) / float(1 << 22), np.unique(vals)
+
+
+def test_sr_full_rounds_up_with_chance_p22():
+    """Full-resolution stochastic rounding: over all 2^22 draw values exactly
+    floor(p * 2^22) round up, so the chance is p when p has at most 22 fractional bits
+    (every value at or above 1, e.g. on [2, 3) where p = |v| - 2) and p truncated to
+    22 bits below 1.  No dead zone: p = 2^-22 rounds up for exactly one draw value,
+    p = 1 - 2^-22 for all but one."""
+    for p in (2.0 ** -22, 2.0 ** -21, 1 / 1024, 1 / 512, 0.3 - 0.3 % 2.0 ** -21,
+              511 / 512 + 2.0 ** -20, 1 - 2.0 ** -22):
+        v = 2.0 + p
+        assert np.float64(np.float32(v)) == v
+        chance, vals = _sr_full_chance(v)
+        assert chance == p, (p, chance)
+        assert set(vals) <= {2.0, 3.0}
+    # below 1 the position has more than 22 bits: the chance is p truncated
+    v = float(np.float32(0.5 + 2.0 ** -10 + 2.0 ** -24))        # p = 2^-9 + 2^-23
+    chance, _ = _sr_full_chance(v)
+    assert chance == 2.0 ** -9
+    # grid values never move; 6 and above give 6
+    for g in F.E2M1_GRID:
+        chance, vals = _sr_full_chance(g)
+        assert chance == 0.0 and list(vals) == [g]
+    codes = N.e2m1_sr_full_code(np.array([6.0, 7.5, 1e30]), np.array([0, 2 ** 32 - 1, 12345], dtype=np.uint32))
+    assert np.all(F.E2M1_GRID[codes] == 6.0)
+
+
+def test_sr_full_has_no_dead_zone_where_8_bit_draws_have_one():
+    """A value 1/1024 of a grid step above a grid point: the 8-bit draws never round it
+    up (bias -1/1024 step), the full-resolution draws round it up for 1/1024 of the
+    draws (no bias)."""
+    v = 2.0 + 1 / 1024
+    k = np.arange(256)
+    assert np.all(F.E2M1_GRID[N.e2m1_sr_code(np.full(256, v), k)] == 2.0)
+    chance, _ = _sr_full_chance(v)
+    assert chance == 1 / 1024
+
+
+def test_sr_full_tensor_is_unbiased_where_8_bit_is_not():
+    """Quantizing a tensor whose values sit 1/1024 of a grid step above grid points:
+    with 8-bit draws the dequantized mean stays on the grid points (biased low); with
+    full-resolution draws it moves up by about 1/1024 of a step."""
+    t = F32(1.0)
+    # block {6, 2 + 1/1024 x 15} at t = 1: candidate 6 has d = 1 exactly (S = 1.0)
+    blocks = np.full((4096, 16), 2.0 + 1 / 1024, dtype=F32)
+    blocks[:, 0] = 6.0
+    ids = np.arange(4096, dtype=np.uint64)
+    q8, _, _, _, _ = N.quantize_blocks(blocks, t, "6", N.sr_bytes(ids, 5, 0))
+    qf, _, _, _, _ = N.quantize_blocks(blocks, t, "6", N.sr_words(ids, 5, 0))
+    v8 = F.E2M1_GRID[q8[:, 1:] & 7]
+    vf = F.E2M1_GRID[qf[:, 1:] & 7]
+    assert np.all(v8 == 2.0)
+    n = vf.size
+    ups = np.count_nonzero(vf == 3.0)
+    assert np.all((vf == 2.0) | (vf == 3.0))
+    # 61440 draws at chance 1/1024: mean 60, sd ~7.7
+    assert abs(ups - n / 1024) < 5 * np.sqrt(n / 1024)
 
 
 def test_sr_tensor_mean_close_to_input():

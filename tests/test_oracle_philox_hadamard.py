@@ -16,7 +16,7 @@ import scipy.linalg
 import torch
 
 from oracle.hadamard import rht_blocks, rht_signs
-from oracle.nvfp4 import sr_bytes
+from oracle.nvfp4 import sr_bytes, sr_words
 from oracle.philox import philox4x32_10, split_seed
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,18 @@ def test_sr_bytes_layout_matches_counter_mapping(torch_philox):
         got = sr_bytes(np.array([b], dtype=np.uint64), 1234, s)[0]
         want = [(words[i // 4] >> (8 * (i % 4))) & 0xFF for i in range(16)]
         assert list(got) == want
+
+
+def test_sr_words_layout_matches_counter_mapping(torch_philox):
+    # full-resolution draws: element i of block b (stream s) takes word i % 4 of the
+    # call with counter (b_lo, b_hi, i // 4, s): torch's offset = b, subsequence =
+    # (i // 4) + (s << 32)
+    for b, s in [(0, 0), (9, 1), ((1 << 35) + 3, 0)]:
+        got = sr_words(np.array([b], dtype=np.uint64), 4321, s)[0]
+        want = []
+        for j in range(4):
+            want += torch_philox(4321, j + (s << 32), b)
+        assert [int(w) for w in got] == want
 
 
 def test_philox_bytes_uniform():
