@@ -705,6 +705,8 @@ def main():
         kernels = {"c2_kernel": ("c2", {}), "c2_step": ("c2", {}),
                    "c3_kernel": ("c3", {"outputs": ("row", "col")}),
                    "c4a_kernel": ("c4a", {"hadamard_seed": 0, "rounding": "sr", "sr_seed": 1234}),
+                   "c4a_full_kernel": ("c4a", {"hadamard_seed": 0, "rounding": "sr_full",
+                                               "sr_seed": 1234}),
                    "c4b_kernel": ("c4b", {"block": "2d"})}
         if args.only not in kernels:
             raise SystemExit(f"unknown --only {args.only}")
@@ -736,6 +738,11 @@ def main():
     rows["c4a_rht_sr"] = bench_quant(fos, "c4a gradient 8192x4096, Hadamard + stochastic rounding",
                                      W.make("c4a"), {"hadamard_seed": 0, "rounding": "sr",
                                                      "sr_seed": 1234}, args.steps, args.warmup)
+    log("C4a with full-resolution stochastic rounding ...")
+    rows["c4a_rht_sr_full"] = bench_quant(fos, "c4a gradient 8192x4096, Hadamard + full-resolution "
+                                          "stochastic rounding", W.make("c4a"),
+                                          {"hadamard_seed": 0, "rounding": "sr_full",
+                                           "sr_seed": 1234}, args.steps, args.warmup)
     log("C4a inverse-Hadamard dequantize ...")
     rows["c4a_dequantize_hadamard_bf16"] = bench_dequant_hadamard(fos, W.make("c4a"), args.steps,
                                                                   args.warmup)

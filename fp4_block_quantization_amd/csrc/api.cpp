@@ -45,7 +45,7 @@ uint32_t hadamard_mask(uint64_t seed) {
 fos_status check_config(const fos_quant_config* cfg) {
   if (!cfg) return FOS_E_NULL;
   if (cfg->struct_size != sizeof(fos_quant_config)) return FOS_E_FLAGS;
-  if (cfg->rule > FOS_RULE_6ONLY || cfg->rounding > FOS_ROUND_STOCHASTIC ||
+  if (cfg->rule > FOS_RULE_6ONLY || cfg->rounding > FOS_ROUND_STOCHASTIC_FULL ||
       cfg->block > FOS_BLOCK_2D || cfg->hadamard > 1)
     return FOS_E_FLAGS;
   if (cfg->outputs == 0 || (cfg->outputs & ~(uint32_t)(FOS_OUT_ROWWISE | FOS_OUT_COLWISE)))
@@ -145,7 +145,7 @@ fos::QuantArgs make_args(const fos_quant_config* cfg, const void* x, int64_t row
   a.sr_k0 = (uint32_t)cfg->sr_seed;
   a.sr_k1 = (uint32_t)(cfg->sr_seed >> 32);
   a.four_over_six = cfg->rule == FOS_RULE_4OVER6;
-  a.sr = cfg->rounding == FOS_ROUND_STOCHASTIC;
+  a.sr = cfg->rounding == FOS_ROUND_STOCHASTIC_FULL ? 2 : cfg->rounding == FOS_ROUND_STOCHASTIC;
   a.two_d = cfg->block == FOS_BLOCK_2D;
   a.rows_out = wants_rows(cfg);
   a.cols_out = wants_cols(cfg);
@@ -370,6 +370,15 @@ fos_status fos_selftest_e2m1_sr(unsigned long long* mismatches, void* stream) {
   if (!mismatches) return FOS_E_NULL;
   if (!aligned(mismatches, 8)) return FOS_E_ALIGN;
   return fos::launch_selftest_e2m1_sr(mismatches, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? FOS_OK
+             : FOS_E_HIP;
+}
+
+fos_status fos_selftest_e2m1_sr_full(unsigned long long* mismatches, void* stream) {
+  if (!mismatches) return FOS_E_NULL;
+  if (!aligned(mismatches, 8)) return FOS_E_ALIGN;
+  return fos::launch_selftest_e2m1_sr_full(mismatches, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? FOS_OK
              : FOS_E_HIP;

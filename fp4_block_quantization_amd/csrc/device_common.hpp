@@ -191,6 +191,35 @@ __device__ __forceinline__ void sr_operands(uint64_t block, uint32_t stream, uin
     r[4 * m + 3] = sr_operand<3>(nw[m]) >> 1;
   }
 }
+// Full-resolution draws: element i of the block takes the whole word i % 4 of the call
+// with counter (b_lo, b_hi, i / 4, stream), four calls per block.  The conversion rounds
+// the first value of a pair up iff p22 * 2^22 + (R >> 10) >= 2^22, and the second under
+// R shifted left by one, so the first position takes the word and the second the word
+// shifted right by one: both then round up iff p22 * 2^22 + (word >> 10) >= 2^22, a
+// chance of exactly p22.  fos_selftest_e2m1_sr_full checks that boundary on the device.
+__device__ __forceinline__ void sr_operands_full(uint64_t block, uint32_t stream, uint32_t k0,
+                                                 uint32_t k1, uint32_t (&r)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 w = philox4x32_10(
+        make_uint4((uint32_t)block, (uint32_t)(block >> 32), (uint32_t)j, stream), k0, k1);
+    r[4 * j + 0] = w.x;
+    r[4 * j + 1] = w.y >> 1;
+    r[4 * j + 2] = w.z;
+    r[4 * j + 3] = w.w >> 1;
+  }
+}
+// Operands of a block's draws for stochastic-rounding mode kSR (1: 8-bit draws, 2: full
+// resolution).
+template <int kSR>
+__device__ __forceinline__ void sr_draws(uint64_t block, uint32_t stream, uint32_t k0,
+                                         uint32_t k1, uint32_t (&r)[16]) {
+  if constexpr (kSR == 2)
+    sr_operands_full(block, stream, k0, k1, r);
+  else
+    sr_operands(block, stream, k0, k1, r);
+}
+
 // Stochastic codes of the pair v = (v0, v1) into byte SEL of `w`, the other three bytes
 // of `w` kept: under v0's operand the byte's low nibble is v0's code, under v1's
 // (shifted) operand its high nibble is v1's code; the other nibble of the byte is then

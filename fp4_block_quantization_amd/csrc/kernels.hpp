@@ -20,7 +20,7 @@ struct QuantArgs {
   uint32_t rht_mask;        // bit k set -> sign k of the Hadamard transform is -1
   uint32_t sr_k0, sr_k1;    // Philox key for stochastic rounding
   bool four_over_six;
-  bool sr;
+  uint8_t sr;               // 0: nearest-even, 1: 8-bit draws, 2: full-resolution draws
   bool two_d;
   bool rows_out, cols_out;
   bool hadamard;
@@ -62,6 +62,11 @@ hipError_t launch_selftest_e2m1(unsigned long long* mismatches, hipStream_t stre
 // rounding to E2M1 under the operands the quantize kernels build from their draws and
 // the draw rule, over every finite fp32 and every draw byte, at both pair positions.
 hipError_t launch_selftest_e2m1_sr(unsigned long long* mismatches, hipStream_t stream);
+
+// Adds to *mismatches the number of disagreements at the rounding boundary of the
+// full-resolution stochastic rounding (operands straight from the draw words), over
+// every finite fp32 at both pair positions.
+hipError_t launch_selftest_e2m1_sr_full(unsigned long long* mismatches, hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* data, const uint8_t* scales, const float* tscale,
                              int64_t rows, int64_t cols, bool bf16_out, void* out,

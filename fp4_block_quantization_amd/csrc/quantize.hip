@@ -82,7 +82,7 @@ __device__ __forceinline__ void store_block(uint8_t* data, uint8_t* scales, int6
 // variant is bound by VALU issue and the extra waves hide its dependent chains.
 constexpr int kRowsPerWG = kThreads;
 
-template <bool k46, bool kSR, bool kRHT>
+template <bool k46, int kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   const int64_t b = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
@@ -102,8 +102,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
   unpack16(w0, w1, v);
   if (kRHT) rht16(v, a.rht_mask);
   uint32_t srr[16];
-  if (kSR) sr_operands((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srr);
-  const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
+  if (kSR) sr_draws<kSR>((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srr);
+  const Cand c = quantize_block<k46, (kSR != 0)>(v, tc.tab, tc.u6, tc.u4, srr);
   store_block_stream(a.row_data, a.row_scales, 8 * b, b, c);
 }
 
@@ -124,7 +124,7 @@ constexpr int kTileC = 64;
 constexpr int kColTileRows = 128;  // rows of a column-wise tile
 constexpr int kRowSub = 4;         // tiles along a row per workgroup with row-wise output
 
-template <int TR, bool k46, bool kSR, bool kRHT, bool kRows>
+template <int TR, bool k46, int kSR, bool kRHT, bool kRows>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
   constexpr int kSub = kRows ? kRowSub : 1;
   constexpr int kIt = TR / 64;          // rows per lane in the load phase
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
         unpack16(w0, w1, v);
         uint32_t srr[16];
         const int64_t blk = gr * (C / 16) + gc / 16;
-        if (kSR) sr_operands((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srr);
-        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
+        if (kSR) sr_draws<kSR>((uint64_t)blk, 0u, a.sr_k0, a.sr_k1, srr);
+        const Cand c = quantize_block<k46, (kSR != 0)>(v, tc.tab, tc.u6, tc.u4, srr);
         rnib[row][4 * s + j] = make_uint2(c.lo, c.hi);
         rsc[row][4 * s + j] = (uint8_t)c.s;
       }
@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
         if (kRHT) rht16(v, a.rht_mask);
         const int64_t blk = col * nrb + gr0 / 16;
         uint32_t srr[16];
-        if (kSR) sr_operands((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srr);
-        const Cand c = quantize_block<k46, kSR>(v, tc.tab, tc.u6, tc.u4, srr);
+        if (kSR) sr_draws<kSR>((uint64_t)blk, 1u, a.sr_k0, a.sr_k1, srr);
+        const Cand c = quantize_block<k46, (kSR != 0)>(v, tc.tab, tc.u6, tc.u4, srr);
         store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
       }
     }
@@ -291,7 +291,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // row hold the 16 rows of one tile (one 16-value row block each), for both tile rows.
 constexpr int k2dTileRows = 2;
 
-template <bool k46, bool kSR, bool kRows, bool kCols>
+template <bool k46, int kSR, bool kRows, bool kCols>
 __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   __shared__ uint2 tr[k2dTileRows][16][17];
   // row-wise outputs of the workgroup, staged so that the global stores cover whole
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
     unpack16(w[2 * q], w[2 * q + 1], v);
     uint32_t srr[16];
     const int64_t rblk = (Rq + row) * tiles_c + T;    // row-wise block id of this row
-    if (kSR) sr_operands((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srr);
+    if (kSR) sr_draws<kSR>((uint64_t)rblk, 0u, a.sr_k0, a.sr_k1, srr);
 
     const float am = row16_max(amax16(v));
     Cand c6, c4;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   }
 }
 
-template <bool k46, bool kSR>
+template <bool k46, int kSR>
 hipError_t dispatch_2d(const QuantArgs& a, hipStream_t s) {
   const int64_t grid = quantize_grid(a);
   if (a.rows_out && a.cols_out)
@@ -429,7 +429,7 @@ hipError_t dispatch_2d(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool k46, bool kSR, bool kRHT>
+template <bool k46, int kSR, bool kRHT>
 hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
   const int64_t grid = quantize_grid(a);
   if (!a.cols_out) {
@@ -444,7 +444,7 @@ hipError_t dispatch_1d(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool k46, bool kSR>
+template <bool k46, int kSR>
 hipError_t dispatch_rule(const QuantArgs& a, hipStream_t s) {
   if (a.two_d) return dispatch_2d<k46, kSR>(a, s);
   return a.hadamard ? dispatch_1d<k46, kSR, true>(a, s) : dispatch_1d<k46, kSR, false>(a, s);
@@ -463,9 +463,12 @@ int64_t quantize_grid(const QuantArgs& a) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
-  if (a.four_over_six)
-    return a.sr ? dispatch_rule<true, true>(a, s) : dispatch_rule<true, false>(a, s);
-  return a.sr ? dispatch_rule<false, true>(a, s) : dispatch_rule<false, false>(a, s);
+  if (a.four_over_six) {
+    if (a.sr == 2) return dispatch_rule<true, 2>(a, s);
+    return a.sr ? dispatch_rule<true, 1>(a, s) : dispatch_rule<true, 0>(a, s);
+  }
+  if (a.sr == 2) return dispatch_rule<false, 2>(a, s);
+  return a.sr ? dispatch_rule<false, 1>(a, s) : dispatch_rule<false, 0>(a, s);
 }
 
 }  // namespace fos

@@ -111,7 +111,64 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_kernel(unsigned lon
   if (bad) atomicAdd(mismatches, (unsigned long long)bad);
 }
 
+// Self-test of the full-resolution stochastic rounding (sr_operands_full): for every
+// finite fp32 v, the position P (22 fractional bits, as in the 8-bit test above) and,
+// at each pair position, the draw words with u = word >> 10 on either side of the
+// boundary P + u = 2^22: u = 2^22 - P must round up (when P > 0) and u = 2^22 - P - 1
+// must not; at 6 and above both draws give 6.  The word's low 10 bits take a pattern
+// from v's bits (the rule ignores them).
+__global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_full_kernel(
+    unsigned long long* mismatches) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint32_t bad = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < ((uint64_t)1 << 32);
+       i += stride) {
+    const uint32_t b = (uint32_t)i;
+    if ((b & 0x7f800000u) == 0x7f800000u) continue;   // NaN, Inf
+    const float v = __uint_as_float(b);
+    const float m = fabsf(v);
+    const uint32_t sign = (b >> 31) << 3;
+    uint32_t lo_code, hi_code, P;
+    if (m >= 6.0f) {
+      lo_code = hi_code = 7u;
+      P = 0u;
+    } else {
+      const float step = (m < 2.0f) ? 0.5f : (m < 4.0f) ? 1.0f : 2.0f;
+      const float y = m / step;
+      const float yl = floorf(y);
+      P = (uint32_t)floorf((y - yl) * 0x1p22f);
+      lo_code = (m < 2.0f) ? (uint32_t)yl : (m < 4.0f) ? 2u + (uint32_t)yl : 6u;
+      hi_code = lo_code + 1u;
+    }
+    const uint32_t low10 = b & 0x3ffu;
+    // u below the boundary (stays down), then on it (rounds up; only when P > 0)
+    const uint32_t u_down = ((1u << 22) - P - 1u) & 0x3fffffu;
+    const uint32_t u_up = ((1u << 22) - P) & 0x3fffffu;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (c == 1 && (P == 0u || m >= 6.0f)) continue;
+      const uint32_t word = ((c ? u_up : u_down) << 10) | low10;
+      const uint32_t expect = (c ? hi_code : lo_code) | sign;
+      const uint32_t w1 = cvt_sr_fp4_byte<0>(0u, f32x2{v, -v}, word);
+      const uint32_t w2 = cvt_sr_fp4_byte<0>(0u, f32x2{-v, v}, word >> 1);
+      bad += ((w1 & 0xfu) != expect) + (((w2 >> 4) & 0xfu) != expect);
+    }
+    if (m >= 6.0f) {   // any draw: 6
+      const uint32_t word = 0xffffffffu;
+      const uint32_t w1 = cvt_sr_fp4_byte<0>(0u, f32x2{v, -v}, word);
+      const uint32_t w2 = cvt_sr_fp4_byte<0>(0u, f32x2{-v, v}, word >> 1);
+      bad += ((w1 & 0xfu) != (7u | sign)) + (((w2 >> 4) & 0xfu) != (7u | sign));
+    }
+  }
+  if (bad) atomicAdd(mismatches, (unsigned long long)bad);
+}
+
 }  // namespace
+
+hipError_t launch_selftest_e2m1_sr_full(unsigned long long* mismatches, hipStream_t s) {
+  selftest_e2m1_sr_full_kernel<<<8192, kThreads, 0, s>>>(mismatches);
+  return hipGetLastError();
+}
 
 hipError_t launch_selftest_e4m3(unsigned long long* mismatches, hipStream_t s) {
   selftest_e4m3_kernel<<<4096, kThreads, 0, s>>>(mismatches);

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfos.so")
 
 FOS_OK, FOS_E_NULL, FOS_E_SHAPE, FOS_E_ALIGN, FOS_E_FLAGS, FOS_E_WORKSPACE, FOS_E_HIP = range(7)
 FOS_RULE_4OVER6, FOS_RULE_6ONLY = 0, 1
-FOS_ROUND_RNE, FOS_ROUND_STOCHASTIC = 0, 1
+FOS_ROUND_RNE, FOS_ROUND_STOCHASTIC, FOS_ROUND_STOCHASTIC_FULL = 0, 1, 2
 FOS_BLOCK_1D, FOS_BLOCK_2D = 0, 1
 FOS_OUT_ROWWISE, FOS_OUT_COLWISE = 1, 2
 FOS_OUT_F32, FOS_OUT_BF16 = 0, 1
@@ -59,6 +59,7 @@ def _load() -> ctypes.CDLL:
         "fos_selftest_e4m3": ([P, P], ctypes.c_int),
         "fos_selftest_e2m1": ([P, P], ctypes.c_int),
         "fos_selftest_e2m1_sr": ([P, P], ctypes.c_int),
+        "fos_selftest_e2m1_sr_full": ([P, P], ctypes.c_int),
         "fos_dequantize": ([P, P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "fos_dequantize_hadamard": ([P, P, P, I64, I64, ctypes.c_uint64, ctypes.c_int, P, P],
                                     ctypes.c_int),
@@ -105,12 +106,13 @@ def make_config(rule: str = "4/6", rounding: str = "rne", block: str = "1d",
                 outputs: Sequence[str] = ("row",), hadamard_seed: Optional[int] = None,
                 sr_seed: Optional[int] = None) -> FosQuantConfig:
     rules = {"4/6": FOS_RULE_4OVER6, "6": FOS_RULE_6ONLY}
-    roundings = {"rne": FOS_ROUND_RNE, "sr": FOS_ROUND_STOCHASTIC}
+    roundings = {"rne": FOS_ROUND_RNE, "sr": FOS_ROUND_STOCHASTIC,
+                 "sr_full": FOS_ROUND_STOCHASTIC_FULL}
     blocks = {"1d": FOS_BLOCK_1D, "2d": FOS_BLOCK_2D}
     out = 0
     for o in outputs:
         out |= {"row": FOS_OUT_ROWWISE, "col": FOS_OUT_COLWISE}[o]
-    if rounding == "sr" and sr_seed is None:
+    if rounding in ("sr", "sr_full") and sr_seed is None:
         raise ValueError("stochastic rounding needs sr_seed")
     return FosQuantConfig(ctypes.sizeof(FosQuantConfig), rules[rule], roundings[rounding],
                           blocks[block], out, 0 if hadamard_seed is None else 1,
@@ -195,6 +197,15 @@ def selftest_e2m1_sr(device="cuda:0") -> int:
     build from their draws, differs from the draw rule; 0 on a correct device."""
     n = torch.zeros(1, dtype=torch.int64, device=device)
     _check(_lib.fos_selftest_e2m1_sr(_ptr(n), _stream(n.device)), "fos_selftest_e2m1_sr")
+    return int(n.item())
+
+
+def selftest_e2m1_sr_full(device="cuda:0") -> int:
+    """Number of disagreements at the rounding boundary of the full-resolution
+    stochastic rounding (every finite fp32 value, both pair positions); 0 on a
+    correct device."""
+    n = torch.zeros(1, dtype=torch.int64, device=device)
+    _check(_lib.fos_selftest_e2m1_sr_full(_ptr(n), _stream(n.device)), "fos_selftest_e2m1_sr_full")
     return int(n.item())
 
 

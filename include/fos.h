@@ -76,7 +76,12 @@ enum { FOS_RULE_4OVER6 = 0, FOS_RULE_6ONLY = 1 };
  * chance n/256, n = number of draw bytes k with (k + 0.5)/256 < p (p taken to 22
  * fractional bits): p <= 1/512 never rounds up, p > 511/512 always does, and the
  * expected result is off by at most 2^-9 of the grid step (plus 2^-22). */
-enum { FOS_ROUND_RNE = 0, FOS_ROUND_STOCHASTIC = 1 };
+enum { FOS_ROUND_RNE = 0, FOS_ROUND_STOCHASTIC = 1, FOS_ROUND_STOCHASTIC_FULL = 2 };
+/* FOS_ROUND_STOCHASTIC_FULL: stochastic rounding with a whole 32-bit Philox4x32-10
+ * word per element (four calls per block; element i of block b takes word i % 4 of
+ * the call with counter (b_lo, b_hi, i / 4, stream)): with u = word >> 10 and P = p's
+ * first 22 fractional bits as an integer, the value rounds up iff P + u >= 2^22, a
+ * chance of p to within 2^-22 and no dead zone near the grid points. */
 /* 1D: 16 consecutive values share a scale.  2D: a 16x16 tile shares one scale and
  * one 4-vs-6 decision; its byte is written into all 16 row-block slots of the tile
  * (the 1D scale layout is kept). */
@@ -221,6 +226,19 @@ fos_status fos_selftest_e2m1(unsigned long long* mismatches, void* stream);
  * 0.  Takes about a second.
  * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
 fos_status fos_selftest_e2m1_sr(unsigned long long* mismatches, void* stream);
+
+/* Self-test of the hardware stochastic rounding to E2M1 as FOS_ROUND_STOCHASTIC_FULL
+ * drives it (operand = the draw word at the first position of a pair, the word
+ * shifted right by one at the second): for every finite fp32 value v and both
+ * positions, the draw words on either side of the rounding boundary -- u = 2^22 - P
+ * (rounds up, when P > 0) and u = 2^22 - P - 1 (stays down), u = word >> 10, P = the
+ * first 22 fractional bits of v's position between its grid neighbours -- must give
+ * the rule's codes (6 and above: 6 for any draw), with the word's low 10 bits set to
+ * an arbitrary pattern.  Since the rounding is monotone in u, this fixes it for every
+ * draw.  Adds the number of disagreements to *mismatches (device uint64, 8-byte
+ * aligned; the caller zeroes it); a correct device gives 0.
+ * Errors: FOS_E_NULL, FOS_E_ALIGN, FOS_E_HIP. */
+fos_status fos_selftest_e2m1_sr_full(unsigned long long* mismatches, void* stream);
 
 /* Dequantize one NVFP4 record (Ultralytics glossary "FP4", "How FP4 works": a value
  * is its E2M1 code times its block's E4M3 scale times the tensor's FP32 scale):

@@ -121,7 +121,7 @@ def q(c, x=FAKE, rows=64, cols=64, rd=FAKE, rs=FAKE, cd=FAKE, cs=FAKE, t=FAKE, w
     ({}, dict(wsb=4), fos.FOS_E_WORKSPACE),
     ({}, dict(ws=ctypes.c_void_p(0x100008)), fos.FOS_E_WORKSPACE),   # not 16-byte aligned
     (dict(raw={"rule": 7}), {}, fos.FOS_E_FLAGS),
-    (dict(raw={"rounding": 2}), {}, fos.FOS_E_FLAGS),
+    (dict(raw={"rounding": 3}), {}, fos.FOS_E_FLAGS),
     (dict(raw={"outputs": 0}), {}, fos.FOS_E_FLAGS),
     (dict(raw={"outputs": 4}), {}, fos.FOS_E_FLAGS),
     (dict(raw={"struct_size": 8}), {}, fos.FOS_E_FLAGS),
@@ -213,6 +213,8 @@ def test_selftest_validation():
     assert L.fos_selftest_e2m1(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
     assert L.fos_selftest_e2m1_sr(None, None) == fos.FOS_E_NULL
     assert L.fos_selftest_e2m1_sr(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
+    assert L.fos_selftest_e2m1_sr_full(None, None) == fos.FOS_E_NULL
+    assert L.fos_selftest_e2m1_sr_full(ctypes.c_void_p(0x100004), None) == fos.FOS_E_ALIGN
 
 
 def test_qlinear_act_validation():

@@ -38,13 +38,14 @@ def _weight_record(fos, wb, cfg):
 def _kwargs(cfg):
     return dict(rule=cfg.rule, rounding=cfg.rounding, block=cfg.block,
                 hadamard_seed=cfg.hadamard_seed if cfg.hadamard else None,
-                sr_seed=cfg.sr_seed if cfg.rounding == "sr" else None)
+                sr_seed=cfg.sr_seed if cfg.rounding in ("sr", "sr_full") else None)
 
 
 ACT_CFGS = {
     "4/6": N.Config(),
     "6": N.Config(rule="6"),
     "sr": N.Config(rounding="sr", sr_seed=4321),
+    "sr_full": N.Config(rounding="sr_full", sr_seed=4323),
     "2d": N.Config(block="2d"),
     "rht": N.Config(hadamard=True, hadamard_seed=29),
 }
