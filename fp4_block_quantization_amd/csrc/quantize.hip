@@ -298,14 +298,15 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   // lines: [tile row][row][tile] nibbles (a row of 16 tiles is 128 contiguous bytes)
   // and scale bytes (16 contiguous bytes).  Stored directly, each wave instruction
   // wrote 16 rows x 32 bytes of nibbles and 16 rows x 4 bytes of scales; staged, 8
-  // threads write one 128-byte line, with non-temporal stores like the row-wise kernel.
+  // threads write one 128-byte line of nibbles with non-temporal stores like the
+  // row-wise kernel, and one thread a row's 16 scale bytes.
   __shared__ uint2 rnib[kRows ? k2dTileRows : 1][16][16];
   __shared__ uint8_t rsc[kRows ? k2dTileRows : 1][16][16];
   const int64_t R = a.rows, C = a.cols;
   const uint32_t tiles_c = (uint32_t)(C / 16);
   const uint32_t wg_per_row = (tiles_c + 15) / 16;
   // neighbouring workgroups share the lines of the row-wise scales (16 bytes each of a
-  // 128-byte line): XCD-contiguous numbering (3% faster at 12288 x 4096)
+  // 128-byte line): XCD-contiguous numbering, so that one L2 merges them
   const uint32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
   const int64_t R0 = (int64_t)(wg / wg_per_row) * (16 * k2dTileRows);
   const int tid = threadIdx.x;
@@ -408,7 +409,10 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
         if (T0 + 16 <= tiles_c && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
           typedef uint32_t v4u __attribute__((ext_vector_type(4)));
           const uint4 sv = *reinterpret_cast<const uint4*>(&rsc[qs][rs][0]);
-          __builtin_nontemporal_store(v4u{sv.x, sv.y, sv.z, sv.w}, reinterpret_cast<v4u*>(dst));
+          // a cached store: the 8 workgroups that share this 128-byte line run on one XCD
+          // (xcd_contiguous), whose L2 merges the pieces (non-temporal 16-byte pieces
+          // each cost a 32-byte write: 1.11x the kernel's output bytes instead of 1.00x)
+          *reinterpret_cast<v4u*>(dst) = v4u{sv.x, sv.y, sv.z, sv.w};
         } else {
           for (uint32_t t = 0; t < 16 && T0 + t < tiles_c; ++t) dst[t] = rsc[qs][rs][t];
         }
