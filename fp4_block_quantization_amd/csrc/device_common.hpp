@@ -244,7 +244,7 @@ __device__ __forceinline__ uint32_t cvt_sr_fp4_byte(uint32_t w, f32x2 v, uint32_
 // its value does not matter and no instruction sets it.
 __device__ __forceinline__ uint32_t any_word() {
   uint32_t w;
-  asm("" : "=v"(w));
+  asm volatile("" : "=v"(w));   // volatile: each call its own register, no copies
   return w;
 }
 

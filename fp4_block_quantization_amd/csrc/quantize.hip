@@ -86,15 +86,14 @@ template <bool k46, int kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   const int64_t b = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
-  uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-  if (b < nblk) {
-    // input read once: non-temporal loads
-    const v4u* xv = reinterpret_cast<const v4u*>(a.x);
-    const v4u l0 = __builtin_nontemporal_load(xv + 2 * b);
-    const v4u l1 = __builtin_nontemporal_load(xv + 2 * b + 1);
-    w0 = make_uint4(l0.x, l0.y, l0.z, l0.w);
-    w1 = make_uint4(l1.x, l1.y, l1.z, l1.w);
-  }
+  // input read once: non-temporal loads.  Lanes past the last block (nblk >= 1: empty
+  // tensors launch nothing) load the last block again and store nothing.
+  const int64_t bl = b < nblk ? b : nblk - 1;
+  const v4u* xv = reinterpret_cast<const v4u*>(a.x);
+  const v4u l0 = __builtin_nontemporal_load(xv + 2 * bl);
+  const v4u l1 = __builtin_nontemporal_load(xv + 2 * bl + 1);
+  const uint4 w0 = make_uint4(l0.x, l0.y, l0.z, l0.w);
+  const uint4 w1 = make_uint4(l1.x, l1.y, l1.z, l1.w);
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab);
   if (b >= nblk) return;
