@@ -34,18 +34,46 @@ struct TensorConsts {
   float u6, u4;
 };
 
+// The inputs of the tensor scale -- this thread's four of the scale pass's partial
+// maxima, or the caller's t -- loaded before the kernel's own input.  Vector loads
+// complete in the order they are issued, so the wait for these leaves the input loads
+// in flight during the workgroup's set-up; loaded after the input, as before, the
+// set-up waited for the input too (2D kernel 28.5 -> 25.2 us, row + column tile
+// kernel 29.4 -> 28.5 us at their bench shapes).
+struct TensorPre {
+  uint32_t p[4];
+  float t;
+};
+constexpr int kRawBufferWord3 = 0x00020000;   // gfx9 raw buffer, 32-bit data format
+__device__ __forceinline__ TensorPre tensor_prefetch(const QuantArgs& a) {
+  TensorPre pre;
+  // The partial maxima through a buffer resource, with no branch around the loads (a
+  // branch made the compiler wait for them at its join, before the input loads): the
+  // buffer holds no bytes when there are no partials, and dwords past its end read 0,
+  // the neutral value of the maximum.
+  const int bytes = a.partials ? 4 * a.npartials : 0;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.partials, 0, bytes, kRawBufferWord3);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    pre.p[k] = __builtin_amdgcn_raw_buffer_load_b32(r, 16u * threadIdx.x + 4 * k, 0, 0);
+  pre.t = a.partials ? 0.0f : a.tscale[0];
+  return pre;
+}
+
 // t from the caller's device scalar, or (fused finish of the tensor-scale pass)
 // from the pass's partial maxima, reduced by every workgroup; workgroup 0 stores t.
 // Then the workgroup's scale table.  Every thread of the workgroup must call this
-// (it synchronizes the workgroup); callers issue their input loads first so that
-// this overlaps them.
-__device__ __forceinline__ TensorConsts tensor_consts(const QuantArgs& a, float2* tab) {
+// (it synchronizes the workgroup).
+__device__ __forceinline__ TensorConsts tensor_consts(const QuantArgs& a, float2* tab,
+                                                      const TensorPre& pre) {
   float t;
   if (a.partials) {
-    t = reduce_partials(a.partials, a.npartials) / kScaleDenom;
+    const uint32_t m = max(max(pre.p[0], pre.p[1]), max(pre.p[2], pre.p[3]));
+    t = __uint_as_float(block_max_u32(m)) / kScaleDenom;
     if (blockIdx.x == 0 && threadIdx.x == 0) a.tscale_out[0] = t;
   } else {
-    t = a.tscale[0];
+    t = pre.t;
   }
   build_scale_table(tab, t);
   TensorConsts c;
@@ -86,6 +114,7 @@ template <bool k46, int kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   const int64_t b = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
+  const TensorPre pre = tensor_prefetch(a);
   // input read once: non-temporal loads.  Lanes past the last block (nblk >= 1: empty
   // tensors launch nothing) load the last block again and store nothing.
   const int64_t bl = b < nblk ? b : nblk - 1;
@@ -94,8 +123,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
   const v4u l1 = __builtin_nontemporal_load(xv + 2 * bl + 1);
   const uint4 w0 = make_uint4(l0.x, l0.y, l0.z, l0.w);
   const uint4 w1 = make_uint4(l1.x, l1.y, l1.z, l1.w);
+  __builtin_amdgcn_sched_barrier(0);   // keep the set-up after the input loads
   __shared__ float2 tab[kScaleTableSize];
-  const TensorConsts tc = tensor_consts(a, tab);
+  const TensorConsts tc = tensor_consts(a, tab, pre);
   if (b >= nblk) return;
   float v[16];
   unpack16(w0, w1, v);
@@ -150,19 +180,19 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
 #pragma unroll
     for (int k = 0; k < kIt; ++k) {
       const int row = (tid >> 2) + 64 * k;
-      const int64_t gr = R0 + row, gc = C0 + 16 * j;
-      w[2 * k] = make_uint4(0, 0, 0, 0);
-      w[2 * k + 1] = w[2 * k];
-      if (gr < R && gc < C) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
-        w[2 * k] = p[0];
-        w[2 * k + 1] = p[1];
-      }
+      // rows and columns past the tensor load its last row / 16 columns (no branch);
+      // their values are never quantized or stored
+      const int64_t gr = min(R0 + row, R - 1), gc = min(C0 + 16 * j, C - 16);
+      const uint4* p = reinterpret_cast<const uint4*>(a.x + gr * C + gc);
+      w[2 * k] = p[0];
+      w[2 * k + 1] = p[1];
     }
   };
+  const TensorPre pre = tensor_prefetch(a);
   load_tile(CW);
+  __builtin_amdgcn_sched_barrier(0);   // keep the set-up after the input loads
   __shared__ float2 tab[kScaleTableSize];
-  const TensorConsts tc = tensor_consts(a, tab);
+  const TensorConsts tc = tensor_consts(a, tab, pre);
 
 #pragma unroll 1
   for (int s = 0; s < kSub; ++s) {
@@ -313,19 +343,21 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(QuantArgs a) {
   const uint32_t T = (wg % wg_per_row) * 16 + tl;
   const bool valid = T < tiles_c;
 
+  const TensorPre pre = tensor_prefetch(a);
   uint4 w[2 * k2dTileRows];
 #pragma unroll
   for (int q = 0; q < k2dTileRows; ++q) {
-    w[2 * q] = make_uint4(0, 0, 0, 0);
-    w[2 * q + 1] = w[2 * q];
-    if (valid && R0 + 16 * q < R) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.x + (R0 + 16 * q + row) * C + 16 * T);
-      w[2 * q] = p[0];
-      w[2 * q + 1] = p[1];
-    }
+    // tiles past the tensor load its last tile row / column (no branch); their values
+    // are never stored
+    const int64_t rr = min(R0 + 16 * q + row, R - 1);
+    const uint32_t Tc = min(T, tiles_c - 1);
+    const uint4* p = reinterpret_cast<const uint4*>(a.x + rr * C + 16 * (int64_t)Tc);
+    w[2 * q] = p[0];
+    w[2 * q + 1] = p[1];
   }
+  __builtin_amdgcn_sched_barrier(0);   // keep the set-up after the input loads
   __shared__ float2 tab[kScaleTableSize];
-  const TensorConsts tc = tensor_consts(a, tab);
+  const TensorConsts tc = tensor_consts(a, tab, pre);
 
 #pragma unroll
   for (int q = 0; q < k2dTileRows; ++q) {
