@@ -194,10 +194,13 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab, pre);
 
-#pragma unroll 1
-  for (int s = 0; s < kSub; ++s) {
+  // Tiles of this workgroup (uniform), each a row phase (row-wise blocks from registers, the
+  // tile into LDS) and, after a barrier, a column phase from LDS; the next tile's loads go out
+  // before the barrier.  Written as two phase functions over a run-time tile count, the
+  // column-only kernel keeps more of its LDS reads in flight (22.3 -> 21.1 us at 8192x4096).
+  const int nsub = (int)min((int64_t)kSub, (C - CW + kTileC - 1) / kTileC);
+  auto row_phase = [&](int s) {
     const int64_t C0 = CW + (int64_t)kTileC * s;
-    if (C0 >= C) break;                          // uniform across the workgroup
 #pragma unroll
     for (int k = 0; k < kIt; ++k) {
       const int row = (tid >> 2) + 64 * k;
@@ -217,9 +220,9 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
         rsc[row][4 * s + j] = (uint8_t)c.s;
       }
     }
-    if (s + 1 < kSub) load_tile(C0 + kTileC);
-    __syncthreads();
-
+  };
+  auto col_phase = [&](int s) {
+    const int64_t C0 = CW + (int64_t)kTileC * s;
     const int rb = tid % kNRB;
     const int sw = 4 * (rb & 7);
     const int64_t nrb = R / 16;
@@ -247,8 +250,14 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(QuantArgs a) {
         store_block(a.col_data, a.col_scales, 8 * blk, blk, c);
       }
     }
-    // the next tile overwrites the LDS tile; the row-wise flush reads other lanes' rows
-    if (kRows || s + 1 < kSub) __syncthreads();
+  };
+#pragma unroll 1
+  for (int s = 0; s < nsub; ++s) {
+    row_phase(s);
+    if (s + 1 < nsub) load_tile(CW + (int64_t)kTileC * (s + 1));
+    __syncthreads();
+    col_phase(s);
+    __syncthreads();   // the next row phase overwrites the tile; the flush reads other rows
   }
 
   if (kRows) {
