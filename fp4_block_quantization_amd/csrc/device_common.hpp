@@ -174,21 +174,26 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 // (b_lo, b_hi, 0, stream)) is element i's draw k_i; r_i = (~k_i << 24) | 0x7fffff for
 // even i (first position of pair i/2) and that shifted right by one for odd i (second
 // position).
+// (nw = ~(Philox word); fill = 0x7fffff)
 template <int B>
-__device__ __forceinline__ uint32_t sr_operand(uint32_t nw) {   // nw = ~(Philox word)
-  return __builtin_amdgcn_perm(nw, 0x007fffffu, 0x04020100u + ((uint32_t)B << 24));
+__device__ __forceinline__ uint32_t sr_operand(uint32_t nw, uint32_t fill) {
+  return __builtin_amdgcn_perm(nw, fill, 0x04020100u + ((uint32_t)B << 24));
 }
 __device__ __forceinline__ void sr_operands(uint64_t block, uint32_t stream, uint32_t k0,
                                             uint32_t k1, uint32_t (&r)[16]) {
   const uint4 w = philox4x32_10(make_uint4((uint32_t)block, (uint32_t)(block >> 32), 0u, stream),
                                 k0, k1);
   const uint32_t nw[4] = {~w.x, ~w.y, ~w.z, ~w.w};
+  // the fill constant in a vector register: the four selectors can then be scalar operands
+  // (a VOP3 instruction takes at most one scalar operand)
+  uint32_t fill;
+  asm volatile("v_mov_b32 %0, 0x7fffff" : "=v"(fill));
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    r[4 * m + 0] = sr_operand<0>(nw[m]);
-    r[4 * m + 1] = sr_operand<1>(nw[m]) >> 1;
-    r[4 * m + 2] = sr_operand<2>(nw[m]);
-    r[4 * m + 3] = sr_operand<3>(nw[m]) >> 1;
+    r[4 * m + 0] = sr_operand<0>(nw[m], fill);
+    r[4 * m + 1] = sr_operand<1>(nw[m], fill) >> 1;
+    r[4 * m + 2] = sr_operand<2>(nw[m], fill);
+    r[4 * m + 3] = sr_operand<3>(nw[m], fill) >> 1;
   }
 }
 // Full-resolution draws: element i of the block takes the whole word i % 4 of the call

@@ -113,12 +113,16 @@ constexpr int kRowsPerWG = kThreads;
 template <bool k46, int kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64_t nblk) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  const int64_t b = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x;
+  // Addresses: the workgroup's first block (scalar) plus a 32-bit lane offset.
+  const int64_t b0 = (int64_t)blockIdx.x * kRowsPerWG;
+  const int lane = (int)threadIdx.x;
+  const int last = (int)min(nblk - 1 - b0, (int64_t)(kRowsPerWG - 1));   // >= 0
+  const int64_t b = b0 + lane;
   const TensorPre pre = tensor_prefetch(a);
   // input read once: non-temporal loads.  Lanes past the last block (nblk >= 1: empty
   // tensors launch nothing) load the last block again and store nothing.
-  const int64_t bl = b < nblk ? b : nblk - 1;
-  const v4u* xv = reinterpret_cast<const v4u*>(a.x);
+  const v4u* xv = reinterpret_cast<const v4u*>(a.x) + 2 * b0;
+  const int bl = min(lane, last);
   const v4u l0 = __builtin_nontemporal_load(xv + 2 * bl);
   const v4u l1 = __builtin_nontemporal_load(xv + 2 * bl + 1);
   const uint4 w0 = make_uint4(l0.x, l0.y, l0.z, l0.w);
@@ -126,14 +130,14 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs a, int64
   __builtin_amdgcn_sched_barrier(0);   // keep the set-up after the input loads
   __shared__ float2 tab[kScaleTableSize];
   const TensorConsts tc = tensor_consts(a, tab, pre);
-  if (b >= nblk) return;
+  if (lane > last) return;
   float v[16];
   unpack16(w0, w1, v);
   if (kRHT) rht16(v, a.rht_mask);
   uint32_t srr[16];
   if (kSR) sr_draws<kSR>((uint64_t)b, 0u, a.sr_k0, a.sr_k1, srr);
   const Cand c = quantize_block<k46, (kSR != 0)>(v, tc.tab, tc.u6, tc.u4, srr);
-  store_block_stream(a.row_data, a.row_scales, 8 * b, b, c);
+  store_block_stream(a.row_data + 8 * b0, a.row_scales + b0, 8 * lane, lane, c);
 }
 
 // ------------------------------------------------------------------ column-wise tiles

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void selftest_e2m1_sr_kernel(unsigned lon
       uint32_t w1 = any_word(), w2 = any_word(), expect[4], r;
 #define FOS_SR_CASE(B)                                                                   \
       expect[B] = (((float)(k0 + B) + 0.5f) * 0x1p-8f < p ? hi_code : lo_code) | sign;   \
-      r = sr_operand<B>(nw);                                                             \
+      r = sr_operand<B>(nw, 0x007fffffu);                                                \
       w1 = cvt_sr_fp4_byte<B>(w1, f32x2{v, -v}, r);                                      \
       w2 = cvt_sr_fp4_byte<B>(w2, f32x2{-v, v}, r >> 1);
       FOS_SR_CASE(0) FOS_SR_CASE(1) FOS_SR_CASE(2) FOS_SR_CASE(3)
