@@ -294,8 +294,20 @@ def bench_qlinear(fos, x_cpu, w_cpu, steps, warmup):
     # work, so the untimed warm-up is about 20 ms of GEMMs
     ms = time_loop(fn, max(10, steps // 2), max(30, warmup), 1)
     flops = 2 * M * N * K
-    return {"shape": [M, N, K], "flop": flops, "ms": ms, "TFLOPs": flops / ms / 1e9,
-            "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+    row = {"shape": [M, N, K], "flop": flops, "ms": ms, "TFLOPs": flops / ms / 1e9,
+           "frac": flops / ms / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+    # reference point, not part of the path: torch's dense bf16 matmul of the unquantized
+    # operands at the same shape (the vendor GEMM, no dequantization), same timing loop
+    xb = x_cpu.to(dev)
+    wt = w_cpu.to(dev).t().contiguous()
+    yb = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def fb(i):
+        torch.matmul(xb, wt, out=yb)
+    ms_b = time_loop(fb, max(10, steps // 2), max(30, warmup), 1)
+    row["torch_bf16_matmul_reference"] = {"ms": ms_b, "TFLOPs": flops / ms_b / 1e9,
+                                          "frac": flops / ms_b / 1e9 / FP16_MFMA_PEAK_TFLOPS}
+    return row
 
 
 def bench_qlinear_act(fos, x_cpu, w_cpu, steps, warmup):
@@ -452,12 +464,31 @@ def bench_mx(fos, x_cpu, w_cpu, x2_cpu, steps, warmup):
     if bad[0]:
         raise RuntimeError("an MXFP4 call returned an error status")
     flops = 2 * M * N * K
+    gemm = {"shape": [M, N, K], "flop": flops, "ms": ms_g, "TFLOPs": flops / ms_g / 1e9,
+            "frac_fp4_peak": flops / ms_g / 1e9 / FP4_MFMA_PEAK_TFLOPS}
+    # reference point, not part of the path: torch's scaled matmul (the vendor MXFP4 GEMM)
+    # on the same two records, same timing loop; null where this torch cannot run it
+    try:
+        a4, b4 = aq.data.view(torch.float4_e2m1fn_x2), bq.data.view(torch.float4_e2m1fn_x2)
+        sa, sb = aq.scales.view(torch.float8_e8m0fnu), bq.scales.view(torch.float8_e8m0fnu)
+        yt = torch._scaled_mm(a4, b4.t(), sa.flatten(), sb.flatten(), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        rel = ((yt.float() - y.float()).norm() / y.float().norm()).item()
+
+        def ft(i):
+            torch._scaled_mm(a4, b4.t(), sa.flatten(), sb.flatten(), out_dtype=torch.bfloat16)
+        ms_t = time_loop(ft, max(10, steps // 2), max(30, warmup), 1)
+        gemm["torch_scaled_mm_reference"] = {"ms": ms_t, "TFLOPs": flops / ms_t / 1e9,
+                                             "frac_fp4_peak": flops / ms_t / 1e9 / FP4_MFMA_PEAK_TFLOPS,
+                                             "rel_diff_vs_ours": rel}
+    except (RuntimeError, AttributeError, TypeError) as exc:
+        log(f"torch scaled matmul reference unavailable: {exc}")
+        gemm["torch_scaled_mm_reference"] = None
     return {"quantize_c2": {"bytes": qb, "ms": ms_q, "GBps": qb / ms_q / 1e6,
                             "frac": qb / ms_q / 1e6 / HBM_PEAK_GBS},
             "dequantize_c2_bf16": {"bytes": db, "ms": ms_d, "GBps": db / ms_d / 1e6,
                                    "frac": db / ms_d / 1e6 / HBM_PEAK_GBS},
-            "gemm_c5": {"shape": [M, N, K], "flop": flops, "ms": ms_g, "TFLOPs": flops / ms_g / 1e9,
-                        "frac_fp4_peak": flops / ms_g / 1e9 / FP4_MFMA_PEAK_TFLOPS}}
+            "gemm_c5": gemm}
 
 
 CEILING_LIB = os.path.join(ROOT, "fp4_block_quantization_amd", "libfos_ceiling.so")
