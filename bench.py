@@ -553,6 +553,46 @@ def bench_ceilings(nbytes, steps, warmup):
     return rows
 
 
+def bench_step_ceiling(fos, x_cpu, steps, warmup):
+    """The two-pass step against its own ceiling: the scale pass (fos_tensor_scale) followed
+    by the pattern kernel (the quantize kernel's exact traffic, no arithmetic), and followed
+    by the quantize kernel (fos_quantize_scaled), on the same rotating inputs.  The second
+    pass of each sees its input partly in the memory-side cache, as inside the step."""
+    import ctypes
+    import torch
+    dev = "cuda:0"
+    R, C = x_cpu.shape
+    case = QuantCase(fos, x_cpu, {}, 3)
+    cl = _ceiling_lib()
+    nb = 2 * R * C
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    bad = [0]
+
+    def pattern(i):
+        rd, rs = case.out[i][0], case.out[i][1]
+        bad[0] |= cl.fos_ceiling_pattern(_vp(case.x[i]), nb, _vp(rd), _vp(rs), stream)
+
+    def scale_then_pattern(i):
+        case.scale_only(i)
+        pattern(i)
+
+    def scale_then_quantize(i):
+        case.scale_only(i)
+        case.scaled(i)
+    out = {}
+    for name, fn in (("scale_pass", case.scale_only), ("scale_pass_then_pattern", scale_then_pattern),
+                     ("scale_pass_then_quantize", scale_then_quantize)):
+        settle(fn, case.sets, 0.1)
+        out["ms_" + name] = time_loop(fn, steps, warmup, case.sets)
+    if bad[0] or case.bad:
+        raise RuntimeError("a step-ceiling call returned an error status")
+    out["ms_pattern_in_step"] = out["ms_scale_pass_then_pattern"] - out["ms_scale_pass"]
+    out["ms_quantize_in_step"] = out["ms_scale_pass_then_quantize"] - out["ms_scale_pass"]
+    out["quantize_over_pattern_in_step"] = out["ms_quantize_in_step"] / out["ms_pattern_in_step"]
+    del case
+    return out
+
+
 def cpu_baseline(x_cpu, rows_sample):
     """The oracle, as it stands, on a slice of the weight workload (its own amax)."""
     import numpy as np
@@ -783,6 +823,9 @@ def main():
     log("HBM ceilings ...")
     rows["hbm_ceilings_c2_bytes"] = bench_ceilings(2 * x2.numel(), args.steps, args.warmup)
     log(json.dumps(rows["hbm_ceilings_c2_bytes"]))
+    log("C2 two-pass step against its ceiling ...")
+    rows["c2_step_ceiling"] = bench_step_ceiling(fos, x2, args.steps, args.warmup)
+    log(json.dumps(rows["c2_step_ceiling"]))
     log("C5 qlinear ...")
     rows["c5_qlinear"] = bench_qlinear(fos, W.make("c5_x"), W.make("c5_w"), args.steps, args.warmup)
     log(json.dumps(rows["c5_qlinear"]))
