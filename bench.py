@@ -192,6 +192,13 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.2):
     if settle_s > 0:
         settle(case.step, sets, settle_s)
     ms = time_loop(case.step, steps, warmup, sets)
+    # the same steps replayed from a HIP graph: a check that the eager step is not bound
+    # by the host's launches (reported beside it, not used for the headline)
+    try:
+        ms_step_graph = graph_loop(lambda st: case.on_stream(st, scaled=False), steps, warmup, sets)
+    except RuntimeError as exc:
+        log(f"{name}: step graph capture failed ({exc})")
+        ms_step_graph = None
     ms_k_b2b = time_loop(case.scaled, steps, warmup, sets)
     try:
         ms_k_graph = graph_loop(case.on_stream, steps, warmup, sets)
@@ -208,7 +215,7 @@ def bench_quant(fos, name, x_cpu, cfg_kw, steps, warmup, n_out=1, settle_s=0.2):
     b = quant_bytes(R, C, n_out)
     row = {"workload": name, "shape": [R, C], "options": {k: (list(v) if isinstance(v, tuple) else v)
                                                           for k, v in cfg_kw.items()},
-           "bytes": b, "ms_step": ms, "GBps_step": b / ms / 1e6,
+           "bytes": b, "ms_step": ms, "GBps_step": b / ms / 1e6, "ms_step_graph_replay": ms_step_graph,
            "frac_step": b / ms / 1e6 / HBM_PEAK_GBS,
            "ms_quant_kernel": ms_k, "GBps_quant_kernel": b / ms_k / 1e6,
            "frac_quant_kernel": b / ms_k / 1e6 / HBM_PEAK_GBS,
@@ -676,11 +683,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
-                    help="profiling aid: run one piece (c2_step, c2_kernel, c3_kernel, c4a_kernel, "
-                         "c4b_kernel, c2_dequant_bf16, c2_dequant_f32, c2_mx_dequant_bf16, "
+                    help="profiling aid: run one piece (c2_kernel, c3_kernel, c4a_kernel, c4a_full_kernel, c4b_kernel; "
+                         "the same with _step for the whole step; "
+                         "c2_dequant_bf16, c2_dequant_f32, c2_mx_dequant_bf16, "
                          "c4a_dequant_hadamard_bf16, c5_qlinear, c5_qlinear_act, "
                          "c5_qlinear_act_given, c5_mx_gemm, copy, ceiling_read, ceiling_copy, "
                          "ceiling_pattern) and exit")
+    ap.add_argument("--settle", type=float, default=0.0,
+                    help="with --only <config>_kernel or _step: run it back to back for this many "
+                         "seconds first, so that the clock has settled (adds dispatches to a trace)")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -779,12 +790,17 @@ def main():
                    "c4a_full_kernel": ("c4a", {"hadamard_seed": 0, "rounding": "sr_full",
                                                "sr_seed": 1234}),
                    "c4b_kernel": ("c4b", {"block": "2d"})}
+        # <config>_step: the whole step (scale pass + quantize) of that configuration
+        kernels.update({k.replace("_kernel", "_step"): v for k, v in kernels.items()
+                        if k.endswith("_kernel")})
         if args.only not in kernels:
             raise SystemExit(f"unknown --only {args.only}")
         name, kw = kernels[args.only]
         case = QuantCase(fos, x2 if name == "c2" else W.make(name), kw, 3)
-        fn = case.step if args.only == "c2_step" else case.scaled
+        fn = case.step if args.only.endswith("_step") else case.scaled
         case.step(0); case.step(1); case.step(2)
+        if args.settle > 0:
+            settle(fn, 3, args.settle)
         for i in range(args.steps):
             fn(i % 3)
         torch.cuda.synchronize()
