@@ -596,3 +596,35 @@ def test_random_configurations_match_oracle(fos, i):
     rows, cols, cfg, scale, dist, seed = _random_case(i)
     bits = bits_of(W.random_bf16(rows, cols, seed, dist, scale=scale))
     assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
+
+
+def test_random_configurations_sweep(fos):
+    """2000 further seeds of the same generator in one test (about 15 s); a mismatch names
+    its configuration."""
+    for i in range(200, 2200):
+        rows, cols, cfg, scale, dist, seed = _random_case(i)
+        bits = bits_of(W.random_bf16(rows, cols, seed, dist, scale=scale))
+        try:
+            assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
+        except AssertionError as exc:
+            raise AssertionError(f"random configuration {i}: {rows}x{cols}, {cfg}, scale "
+                                 f"{scale:.3g}, {dist}") from exc
+
+
+def _random_large_case(i):
+    """Seeded random configuration with a larger shape (up to 1100 x 2064): many workgroups
+    of every kernel, several tiles along both dimensions, ragged edges."""
+    rows, cols, cfg, scale, dist, seed = _random_case(10_000 + i)
+    rng = np.random.default_rng(20_000 + i)
+    tiled = cfg.cols_out or cfg.block == "2d"
+    rows = 16 * int(rng.integers(8, 66)) if tiled else int(rng.integers(100, 1101))
+    cols = 16 * int(rng.integers(16, 130))
+    return rows, cols, cfg, scale, dist, seed
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_large_configurations_match_oracle(fos, i):
+    rows, cols, cfg, scale, dist, seed = _random_large_case(i)
+    print(f"large random configuration {i}: {rows}x{cols}, {cfg}", flush=True)
+    bits = bits_of(W.random_bf16(rows, cols, seed, dist, scale=scale))
+    assert_quant_equal(gpu_quantize(fos, bits, cfg), N.quantize(bits, cfg))
