@@ -611,6 +611,29 @@ def test_random_configurations_sweep(fos):
                                  f"{scale:.3g}, {dist}") from exc
 
 
+def test_random_records_dequantize_sweep(fos):
+    """Dequantize, on the GPU, the oracle's records of 300 seeded random configurations
+    (every layout each produces; fp32 and bf16 outputs; through the inverse Hadamard
+    transform where the record was transformed): bit-exact against the oracle."""
+    for i in range(300):
+        rows, cols, cfg, scale, dist, seed = _random_case(5_000 + i)
+        o = N.quantize(bits_of(W.random_bf16(rows, cols, seed, dist, scale=scale)), cfg)
+        for lay in [l for l, on in (("row", cfg.rows_out), ("col", cfg.cols_out)) if on]:
+            q = _dev_record(fos, o, lay)
+            data, scales = o[f"{lay}_data"], o[f"{lay}_scales"]
+            what = f"random record {i} ({lay}, {rows}x{cols}, {cfg})"
+            want = N.dequantize(data, scales, o["t"])
+            assert_same_bytes(fos.dequantize(q, torch.float32).cpu().numpy().view(np.uint32),
+                              want.view(np.uint32), what + " fp32")
+            assert_same_bytes(bits_of(fos.dequantize(q, torch.bfloat16).cpu()),
+                              F.f32_to_bf16_bits(want), what + " bf16")
+            if cfg.hadamard:
+                q.hadamard_seed = cfg.hadamard_seed
+                want = N.dequantize_hadamard(data, scales, o["t"], cfg.hadamard_seed)
+                got = fos.dequantize(q, torch.float32, inverse_hadamard=True).cpu().numpy()
+                assert_same_bytes(got.view(np.uint32), want.view(np.uint32), what + " inverse")
+
+
 def _random_large_case(i):
     """Seeded random configuration with a larger shape (up to 1100 x 2064): many workgroups
     of every kernel, several tiles along both dimensions, ragged edges."""
