@@ -105,6 +105,25 @@ def test_mx_gemm_matches_fp64_reference(fos, m, n, k):
     _gemm_check(y, oa, ob)
 
 
+@pytest.mark.parametrize("i", range(16))
+def test_mx_gemm_random_shapes(fos, i):
+    """Seeded random shapes (ragged in M and N, K a multiple of 256) and value ranges:
+    within the tolerance of the fp64 reference of the same MXFP4 records."""
+    rng = np.random.default_rng(50_000 + i)
+    m, n, k = int(rng.integers(1, 700)), int(rng.integers(1, 700)), 256 * int(rng.integers(1, 7))
+    ab = bits_of(W.random_bf16(m, k, int(rng.integers(0, 2 ** 31)), ("normal", "student_t")[i % 2],
+                               scale=float(10.0 ** rng.uniform(-6, 6))))
+    bb = bits_of(W.random_bf16(n, k, int(rng.integers(0, 2 ** 31)), "normal",
+                               scale=float(10.0 ** rng.uniform(-6, 6))))
+    oa, ob = MX.quantize(ab), MX.quantize(bb)
+    print(f"mx gemm random {i}: {m}x{n}x{k}", flush=True)
+    dev = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    aq = fos.MXFP4Tensor(dev(oa["data"]), dev(oa["scales"]))
+    bq = fos.MXFP4Tensor(dev(ob["data"]), dev(ob["scales"]))
+    y = bits_of(fos.mx_qlinear_fwd(aq, bq).cpu())
+    _gemm_check(y, oa, ob)
+
+
 def test_mx_gemm_full_size_c5_sampled(fos):
     """The c5 shape (8192 x 12288 x 4096) quantized and multiplied on the GPU; sampled
     rows and columns against the oracle's quantization of those rows."""

@@ -424,6 +424,26 @@ def test_qlinear_matches_fp64_reference(fos, m, n, k):
     _qlinear_check(y, ox["row_data"], ox["row_scales"], ox["t"], ow["row_data"], ow["row_scales"], ow["t"])
 
 
+@pytest.mark.parametrize("i", range(24))
+def test_qlinear_random_shapes(fos, i):
+    """Seeded random shapes (ragged in M and N, K a multiple of 64), random value ranges and
+    quantization options of both operands (W 1D or 2D): within the tolerance of the fp64
+    reference of the same records, element-wise bound included."""
+    rng = np.random.default_rng(40_000 + i)
+    m, n, k = int(rng.integers(1, 700)), 16 * int(rng.integers(1, 45)), 64 * int(rng.integers(1, 25))
+    cx = N.Config(rule=("4/6", "6")[int(rng.random() < 0.25)],
+                  rounding=("rne", "sr")[int(rng.random() < 0.4)], sr_seed=int(rng.integers(0, 2 ** 62)))
+    cw = N.Config(block=("1d", "2d")[int(rng.random() < 0.4)])
+    xb = bits_of(W.random_bf16(m, k, int(rng.integers(0, 2 ** 31)), ("normal", "student_t")[i % 2],
+                               scale=float(10.0 ** rng.uniform(-6, 6))))
+    wb = bits_of(W.random_bf16(n, k, int(rng.integers(0, 2 ** 31)), "normal",
+                               scale=float(10.0 ** rng.uniform(-6, 6))))
+    ox, ow = N.quantize(xb, cx), N.quantize(wb, cw)
+    print(f"qlinear random {i}: {m}x{n}x{k}, X {cx}, W {cw}", flush=True)
+    y = bits_of(fos.qlinear_fwd(_dev_record(fos, ox, "row"), _dev_record(fos, ow, "row")).cpu())
+    _qlinear_check(y, ox["row_data"], ox["row_scales"], ox["t"], ow["row_data"], ow["row_scales"], ow["t"])
+
+
 def test_qlinear_full_size_c5_sampled(fos, workloads):
     xb, wb = workloads("c5_x"), workloads("c5_w")
     cfg = N.Config()
