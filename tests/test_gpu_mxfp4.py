@@ -92,6 +92,27 @@ def _gemm_check(y_bits, a, b):
     assert np.all(np.abs(yg - y64) <= bound), np.max(np.abs(yg - y64) / bound)
 
 
+def test_mx_random_sweep(fos):
+    """300 seeded random shapes (rows 1 to 400, columns a multiple of 32 up to 2048) and
+    value ranges: MXFP4 records bit-exact, and their dequantization (fp32, bf16) too."""
+    for i in range(300):
+        rng = np.random.default_rng(60_000 + i)
+        R, C = int(rng.integers(1, 401)), 32 * int(rng.integers(1, 65))
+        dist = ("normal", "student_t", "uniform")[i % 3]
+        bits = bits_of(W.random_bf16(R, C, int(rng.integers(0, 2 ** 31)), dist,
+                                     scale=float(10.0 ** rng.uniform(-30, 30))))
+        what = f"random MXFP4 case {i}: {R}x{C}, {dist}"
+        q = fos.mx_quantize(to_gpu(bits))
+        o = MX.quantize(bits)
+        assert np.array_equal(q.data.cpu().numpy(), o["data"]), what
+        assert np.array_equal(q.scales.cpu().numpy(), o["scales"]), what
+        want = MX.dequantize(o["data"], o["scales"])
+        got = fos.mx_dequantize(q, torch.float32).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), what
+        got16 = bits_of(fos.mx_dequantize(q, torch.bfloat16).cpu())
+        assert np.array_equal(got16, F.f32_to_bf16_bits(want)), what
+
+
 @pytest.mark.parametrize("m,n,k", [(256, 256, 256), (512, 768, 512), (200, 72, 256),
                                    (300, 520, 1024), (1024, 768, 2048), (1, 16, 256)])
 def test_mx_gemm_matches_fp64_reference(fos, m, n, k):
