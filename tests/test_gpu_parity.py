@@ -476,9 +476,23 @@ def _dev_record(fos, o, lay):
 def test_qlinear_bwd_matches_fp64_reference(fos, m, n, k):
     """dX = deq(dY) deq(W^T)^T and dW = deq(dY^T) deq(X^T)^T from the oracle's records
     (dY with stochastic rounding, W with 2D blocks, as in training)."""
-    xb = bits_of(W.random_bf16(m, k, 3 * m + k, "student_t"))
-    wb = bits_of(W.random_bf16(n, k, n + 5 * k, "normal", scale=0.02))
-    gb = bits_of(W.random_bf16(m, n, m + 7 * n, "normal", scale=1e-3))
+    _check_bwd(fos, m, n, k, (3 * m + k, n + 5 * k, m + 7 * n))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_qlinear_bwd_random_shapes(fos, i):
+    """The backward products at seeded random shapes (M and N multiples of 64, the inner
+    dimensions of dW and dX; K a multiple of 16)."""
+    rng = np.random.default_rng(70_000 + i)
+    m, n, k = 64 * int(rng.integers(1, 11)), 64 * int(rng.integers(1, 13)), 16 * int(rng.integers(1, 61))
+    print(f"qlinear backward random {i}: {m}x{n}x{k}", flush=True)
+    _check_bwd(fos, m, n, k, tuple(int(v) for v in rng.integers(0, 2 ** 31, 3)))
+
+
+def _check_bwd(fos, m, n, k, seeds):
+    xb = bits_of(W.random_bf16(m, k, seeds[0], "student_t"))
+    wb = bits_of(W.random_bf16(n, k, seeds[1], "normal", scale=0.02))
+    gb = bits_of(W.random_bf16(m, n, seeds[2], "normal", scale=1e-3))
     ox = N.quantize(xb, N.Config(cols_out=True))
     ow = N.quantize(wb, N.Config(cols_out=True, block="2d"))
     og = N.quantize(gb, N.Config(cols_out=True, rounding="sr", sr_seed=77))
